@@ -1,0 +1,55 @@
+"""Planted mistakes in the oracle must fail a pin.
+
+Each mutant is a copy of oracle.c with one plausible error (a dropped term,
+a wrong rounding rule, a wrong constant, a wrong index, a flipped sign),
+compiled on the CPU into a temporary library. The pins are run against it;
+at least one must fail, otherwise the pins would not catch that mistake.
+"""
+import os
+
+import pytest
+
+import oracle
+from tests import oracle_pins as P
+
+MUTANTS = {
+    "drop_act_scale": ("t = t * xs[m];", ""),
+    "drop_w_scale_f64": ("* (double)ws[n];", ";"),
+    "round_half_away": ("t = rintf(t);", "t = roundf(t);"),
+    "scale_128": ("float s = a / 127.0f;", "float s = a / 128.0f;"),
+    "inv_128": ("float inv = 127.0f / a;", "float inv = 128.0f / a;"),
+    "absmax_no_abs": ("float m = fabsf(v[k]);", "float m = v[k];"),
+    "truncate_not_round": ("t = rintf(t);", "t = truncf(t);"),
+    "no_zero_row_rule": ("if (a < 0x1p-100f) {\n        *scale = 0.0f;",
+                         "if (a < 0.0f) {\n        *scale = 0.0f;"),
+    "gemm_wrong_b_row": ("const int8_t *br = b + n * ldb;", "const int8_t *br = b + (N - 1 - n) * ldb;"),
+    "gemm_short_k": ("for (int64_t k = 0; k < K; ++k)\n                s +=",
+                     "for (int64_t k = 0; k + 1 < K; ++k)\n                s +="),
+    "gemm_rows_ignored": ("a + (rows ? rows[i] : i) * lda", "a + i * lda"),
+    "bias_subtracted": ("t = t + bf16_bits_to_float(bias[n]);", "t = t - bf16_bits_to_float(bias[n]);"),
+    "bf16_truncate": ("u += 0x7fffu + lsb;", "u += 0u * lsb;"),
+    "bf16_round_half_up": ("u += 0x7fffu + lsb;", "u += 0x8000u + 0u * lsb;"),
+    "xs_indexed_by_column": ("t = t * xs[m];", "t = t * xs[n % M];"),
+    "f64_double_rounding": ("double r = nearbyint(ldexp(m, 8));", "double r = nearbyint(ldexp((float)m, 8));"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mutated = src.replace(old, new, 1)
+    path = os.path.join(tmp_path, "mutant.c")
+    with open(path, "w") as f:
+        f.write(mutated)
+    lib = oracle.build(path, os.path.join(tmp_path, "libmutant.so"))
+    o = oracle.Oracle(lib)
+    failures = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(o)
+        except (AssertionError, OverflowError, ValueError, IndexError) as e:
+            failures.append(pin.__name__)
+            break
+    assert failures, f"no pin detects mutant {name}"
