@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Benchmark of the W8A8 int8-dynamic linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fused_qkv]
+
+One step is the whole hot path on one batch: the per-token activation quant
+(int8_quant_per_token) followed by the int8 MFMA matmul with its fused
+scale/bias/bf16 epilogue (int8_scaled_mm). The weight is quantized per
+output channel and repacked once, before timing. Inputs are seeded synthetic
+tensors (workloads/), already resident in HBM when the timed region starts.
+
+Printed: one JSON line with the step throughput (int8 TOP/s of 2*M*N*K per
+step), the roofline of the dominant kernel (int8_scaled_mm, its average
+launch duration from HIP events on the launch stream), the quant pass's
+GB/s, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
+PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E, GB/s
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="fused_qkv")
+    p.add_argument("--tile", type=int, default=-1, help="force a matmul tile id (-1 = automatic)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target wall time of the oracle's sampled GEMM")
+    p.add_argument("--no-quant-large", action="store_true",
+                   help="skip the quant bandwidth run on the FFN-down activations")
+    p.add_argument("--only", choices=["step", "mm", "quant"], default=None,
+                   help="launch only this part in a loop (for profiler runs)")
+    return p.parse_args(argv)
+
+
+def world_size() -> int:
+    return int(os.environ.get("WORLD_SIZE", "1"))
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "w8a8_int8_dynamic_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+class Bound:
+    """A libw8a8 entry point with its arguments marshalled once."""
+
+    def __init__(self, fn, *args):
+        self.fn, self.args = fn, args
+
+    def __call__(self):
+        rc = self.fn(*self.args)
+        if rc != 0:
+            from w8a8_int8_dynamic_amd import _lib
+            raise RuntimeError(f"{self.fn.__name__} failed: {_lib.last_error()}")
+
+
+def time_loop(torch, fn, iters: int) -> float:
+    """Average milliseconds per call of fn over iters back-to-back calls, from
+    HIP events recorded on torch's current stream (the launch stream)."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(iters):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def dev_bf16(torch, bits: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def cpu_baseline(w, inp, target_s: float) -> dict:
+    """The oracle (as it stands) on a bounded sample of the workload.
+
+    Times the full per-token quant, then the exact int32 GEMM and the epilogue
+    on a sample of token rows sized to take about target_s seconds, and scales
+    the GEMM/epilogue time to all M rows. Returns int8 TOP/s of 2*M*N*K.
+    """
+    import oracle
+    o = oracle.load()
+    wq, ws = o.quant_per_channel(inp.w_f32)        # offline weight prep, not timed
+    t0 = time.perf_counter()
+    xq, xs = o.quant_per_token(inp.x_bf16)
+    t_quant = time.perf_counter() - t0
+    rng = np.random.default_rng(w.seed)
+    probe = np.sort(rng.choice(w.M, min(w.M, 4), replace=False))
+    t0 = time.perf_counter()
+    o.gemm_i32(xq, wq, probe)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    n_rows = int(min(w.M, max(4, target_s / max(per_row, 1e-9))))
+    rows = np.sort(rng.choice(w.M, n_rows, replace=False))
+    t0 = time.perf_counter()
+    acc = o.gemm_i32(xq, wq, rows)
+    t_gemm = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    o.epilogue_f32(acc, xs[rows], ws, inp.bias_bf16)
+    t_epi = time.perf_counter() - t0
+    scale = w.M / n_rows
+    t_total = t_quant + (t_gemm + t_epi) * scale
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {
+        "value": round(w.ops / t_total / 1e12, 6),
+        "unit": "TOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"full per-token quant of X [{w.M},{w.K}] plus exact int32 GEMM and fp32 "
+                   f"epilogue on {n_rows} of {w.M} token rows (x{scale:.2f} to all rows); "
+                   f"{t_quant + t_gemm + t_epi:.1f} s measured"),
+        "seconds_full_step_estimate": round(t_total, 3),
+    }
+
+
+def traffic_record(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, when they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    entry = rec.get(f"{kernel}:{workload}")
+    if not entry or entry.get("source_digest") != source_digest():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1 or world_size() != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world_size()}); this build has no multi-GPU path.", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads as wl
+    from w8a8_int8_dynamic_amd import _lib, ops
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    L = _lib.lib()
+    dev = torch.cuda.current_device()
+    if not ops.device_supported(dev):
+        print("the current device is not gfx950", file=sys.stderr)
+        return 1
+
+    w = wl.by_name(args.workload)
+    M, K, N = w.M, w.K, w.N
+    inp = wl.generate(w)
+    x = dev_bf16(torch, inp.x_bf16)
+    bias = None if inp.bias_bf16 is None else dev_bf16(torch, inp.bias_bf16)
+    wq, ws = ops.quant_per_channel(torch.from_numpy(inp.w_f32).cuda())   # load time
+    packed = ops.prepack_weight(wq)
+    del wq
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    xs = torch.empty((M,), dtype=torch.float32, device="cuda")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    tile = args.tile if args.tile >= 0 else ops.tile_auto(M, N, K)
+
+    quant = Bound(L.int8_quant_per_token, x.data_ptr(), M, K, K, xq.data_ptr(), K, xs.data_ptr(),
+                  stream)
+    mm = Bound(L.int8_scaled_mm_tile, xq.data_ptr(), K, xs.data_ptr(), packed.data_ptr(),
+               ws.data_ptr(), None if bias is None else bias.data_ptr(), M, N, K, 0,
+               out.data_ptr(), N, stream, tile)
+
+    def step():
+        quant()
+        mm()
+
+    if args.only:
+        fn = {"step": step, "mm": mm, "quant": quant}[args.only]
+        for _ in range(args.warmup + args.steps):
+            fn()
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "launches": args.warmup + args.steps,
+                          "workload": w.name, "tile": ops.tile_name(tile)}), flush=True)
+        return 0
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_step = time_loop(torch, step, args.steps)
+    ms_mm = time_loop(torch, mm, args.steps)
+    ms_quant = time_loop(torch, quant, args.steps)
+
+    # Cold variant of the matmul: rotate over weight copies larger than the
+    # 256 MB last-level cache so each launch streams its weight from HBM.
+    copies = max(2, int(np.ceil(512e6 / packed.numel())))
+    cold_packs = [packed.clone() for _ in range(min(copies, 16))]
+    cold_calls = [Bound(L.int8_scaled_mm_tile, xq.data_ptr(), K, xs.data_ptr(), p.data_ptr(),
+                        ws.data_ptr(), None if bias is None else bias.data_ptr(), M, N, K, 0,
+                        out.data_ptr(), N, stream, tile) for p in cold_packs]
+    it = iter(range(1 << 30))
+    ms_mm_cold = time_loop(torch, lambda: cold_calls[next(it) % len(cold_calls)](), args.steps)
+    del cold_packs, cold_calls
+
+    quant_bytes = 3 * M * K + 4 * M
+    mm_ops = 2 * M * N * K
+    mm_min_bytes = M * K + packed.numel() + 4 * M + 4 * N + 2 * M * N + (0 if bias is None else 2 * N)
+    achieved = mm_ops / (ms_mm * 1e-3) / 1e12
+    rec = {
+        "metric": "int8 TOPS + % MFMA peak of quant+scaled_mm at M512 K4096 N12288; quant GB/s",
+        "value": round(mm_ops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded; workloads/ recipe), weights quantized per channel on the GPU",
+        "config": {"workload": w.description, "M": M, "K": K, "N": N,
+                   "bias": bias is not None, "tile": ops.tile_name(tile),
+                   "step": "int8_quant_per_token + int8_scaled_mm (bf16 out)"},
+        "pct_mfma_peak_step": round(100 * mm_ops / (ms_step * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),
+        "scaled_mm": {"us": round(ms_mm * 1e3, 3), "tops": round(achieved, 2),
+                      "us_cold": round(ms_mm_cold * 1e3, 3),
+                      "tops_cold": round(mm_ops / (ms_mm_cold * 1e-3) / 1e12, 2),
+                      "min_hbm_bytes": mm_min_bytes},
+        "quant": {"us": round(ms_quant * 1e3, 3),
+                  "gbps": round(quant_bytes / (ms_quant * 1e-3) / 1e9, 1),
+                  "bytes": quant_bytes},
+        "roofline": {
+            "kernel": "int8_scaled_mm",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TOP/s",
+            "frac": round(achieved / PEAK_INT8_TOPS, 4),
+            "traffic": traffic_record("int8_scaled_mm", w.name),
+        },
+        "source_digest": source_digest(),
+    }
+
+    if not args.no_quant_large:
+        rec["quant_large"] = quant_bandwidth(torch, L, wl, stream, args.steps)
+    del x, xq, xs, out, packed
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def quant_bandwidth(torch, L, wl, stream, steps: int) -> dict:
+    """int8_quant_per_token on the FFN-down activations [8192, 12288], rotating
+    over input/output sets larger than the last-level cache (302 MB moved per
+    launch: bf16 read, int8 codes and fp32 scales written)."""
+    w = wl.by_name("ffn_down")
+    inp = wl.generate(w)
+    M, K = w.M, w.K
+    x0 = dev_bf16(torch, inp.x_bf16)
+    sets = []
+    for i in range(3):
+        x = x0 if i == 0 else x0.clone()
+        sets.append((x, torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                     torch.empty((M,), dtype=torch.float32, device="cuda")))
+    calls = [Bound(L.int8_quant_per_token, x.data_ptr(), M, K, K, q.data_ptr(), K, s.data_ptr(),
+                   stream) for x, q, s in sets]
+    for c in calls:
+        c()
+    it = iter(range(1 << 30))
+    iters = max(10, min(steps, 100))
+    ms = time_loop(torch, lambda: calls[next(it) % len(calls)](), iters)
+    nbytes = 3 * M * K + 4 * M
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    del sets, calls, x0
+    torch.cuda.empty_cache()
+    return {"workload": w.description, "us": round(ms * 1e3, 3), "gbps": round(gbps, 1),
+            "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4), "bytes": nbytes,
+            "buffers": "3 rotating sets (906 MB)"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

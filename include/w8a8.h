@@ -1,0 +1,183 @@
+/*
+ * w8a8.h - C ABI of libw8a8, W8A8 int8-dynamic linear layers on MI355X (gfx950).
+ *
+ * The layer computed here is the one the page "Issue 5 probe: int8 quantized
+ * DiT serve paths on the RTX 3090 (24 GB)" serves in its "Round two" section:
+ * int8 weights quantized per output channel with fp32 scales, activations
+ * quantized per token at run time (dynamic, symmetric), an int8 x int8 ->
+ * int32 matmul, and a scale epilogue back to bf16. The same page's kernel-path
+ * paragraph names the two run-time ops (a per-token quant, then a scaled
+ * matmul) and the load-time transpose-repack of the weight; this header
+ * exposes exactly those three steps, plus the offline weight quantization
+ * that produces the int8 weights and a debug unpack of the repacked weight.
+ *
+ * Conventions for every entry point:
+ *   - Pointers to tensors are DEVICE pointers on the current HIP device.
+ *     bf16 values are passed as their raw 16-bit patterns (uint16_t).
+ *   - Shapes are row-major with an explicit leading dimension (elements
+ *     between consecutive rows). A matrix [R, C] with leading dimension ld
+ *     occupies (R-1)*ld + C elements.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
+ *     and the call returns without synchronizing; inputs must stay alive and
+ *     unmodified until the stream reaches the work.
+ *   - The library never allocates, frees or synchronizes device memory. The
+ *     caller owns every buffer. Outputs must not alias inputs.
+ *   - All argument checks run on the host before any HIP call, so a bad
+ *     argument returns an error without touching the device. There is no
+ *     fallback path: an unsupported device or argument is an error.
+ *   - Calls are thread-safe; the only shared state is a per-device cache of
+ *     the "is this a gfx950" answer and a thread-local error message.
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum w8a8_status {
+    W8A8_OK = 0,
+    W8A8_ERR_NULL = 1,   /* a required pointer is NULL */
+    W8A8_ERR_SHAPE = 2,  /* a size or leading dimension is out of range */
+    W8A8_ERR_ALIGN = 3,  /* a pointer or leading dimension breaks an alignment rule */
+    W8A8_ERR_DEVICE = 4, /* no usable current device, or it is not gfx950 */
+    W8A8_ERR_MODE = 5,   /* unknown output mode or tile id */
+    W8A8_ERR_HIP = 6     /* the HIP runtime reported an error when launching */
+} w8a8_status_t;
+
+/* Output of int8_scaled_mm: the bf16 layer output, or the raw int32
+ * accumulators (debug mode; the scales and bias are then ignored). */
+typedef enum w8a8_mm_out {
+    W8A8_OUT_BF16 = 0,
+    W8A8_OUT_I32 = 1
+} w8a8_mm_out_t;
+
+/* Largest K accepted by int8_scaled_mm: the largest multiple of 16 with
+ * 128 * 128 * K < 2^31, so no int32 partial sum can overflow for any int8
+ * codes (the quantizers only emit -127..127). */
+#define W8A8_MAX_K 131056
+
+/*
+ * int8_quant_per_token - dynamic per-token symmetric activation quantization.
+ * (Page "Issue 5 probe ...", section "Round two": dynamic per-token symmetric
+ * int8 activations; page "Online Quantization", Parameters table: the
+ * "dynamic" activation scheme computes activation scales at run time.)
+ *
+ * For each row m of x [M, ldx] (bf16), over its first K elements:
+ *   a = max_k |x[m,k]|
+ *   if a < 2^-100:  x_scale[m] = 0, xq[m,:] = 0
+ *   else:           x_scale[m] = fl32(a / 127), inv = fl32(127 / a),
+ *                   xq[m,k] = clamp(round_half_even(fl32(x[m,k] * inv)), -127, 127)
+ * Outputs: xq int8 [M, ldq], x_scale fp32 [M].
+ * Requirements: M >= 0 (M == 0 is a no-op), K >= 1, ldx >= K, ldq >= K;
+ * x 16-byte aligned and ldx a multiple of 8; xq 8-byte aligned and ldq a
+ * multiple of 8; x_scale 4-byte aligned. Any K is allowed (ragged tails are
+ * handled element by element). NaN/Inf inputs give unspecified codes.
+ */
+w8a8_status_t int8_quant_per_token(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                                   int8_t *xq, int64_t ldq, float *x_scale, void *stream);
+
+/*
+ * int8_quant_per_channel - per-output-channel symmetric weight quantization.
+ * (Page "Issue 5 probe ...", "Round one" setup paragraph: int8 weights,
+ * per-output-channel symmetric; "Round two" artifacts paragraph: int8 weights
+ * with fp32 per-channel scales. Page "Online Quantization", Overview: online
+ * quantization computes weights and scales while loading.)
+ *
+ * The same rule as int8_quant_per_token applied to each row of an fp32
+ * weight w [N, ldw] (out x in). Outputs: wq int8 [N, ldq], w_scale fp32 [N].
+ * Requirements: N >= 0, K >= 1, ldw >= K, ldq >= K; w 16-byte aligned and
+ * ldw a multiple of 4; wq 8-byte aligned, ldq a multiple of 8.
+ */
+w8a8_status_t int8_quant_per_channel(const float *w, int64_t N, int64_t K, int64_t ldw,
+                                     int8_t *wq, int64_t ldq, float *w_scale, void *stream);
+
+/*
+ * int8_prepack_weight_bytes - size in bytes of the prepacked form of an
+ * int8 weight [N, K]: round_up(N, 16) * round_up(K, 64). Returns 0 when
+ * N < 1, K < 1 or the size does not fit in size_t.
+ */
+size_t int8_prepack_weight_bytes(int64_t N, int64_t K);
+
+/*
+ * int8_prepack_weight - load-time repack of an int8 weight into the layout
+ * int8_scaled_mm reads (page "Issue 5 probe ...", "Round two" kernel-path
+ * paragraph: load, then transpose-repack, then apply).
+ *
+ * A pure byte permutation with zero padding: the packed buffer is a sequence
+ * of 1024-byte fragments F[nb][kb] (nb < round_up(N,16)/16, kb <
+ * round_up(K,64)/64, kb fastest). Byte 16*l + j of F[nb][kb] holds
+ * wq[16*nb + l % 16][64*kb + 16*(l / 16) + j] for l < 64, j < 16, or 0 when
+ * that row or column lies outside [N, K].
+ * Requirements: N >= 1, K >= 1, ldw >= K; w_packed 16-byte aligned with
+ * int8_prepack_weight_bytes(N, K) bytes. wq has no alignment rule.
+ */
+w8a8_status_t int8_prepack_weight(const int8_t *wq, int64_t N, int64_t K, int64_t ldw,
+                                  void *w_packed, void *stream);
+
+/*
+ * int8_unpack_weight - inverse of int8_prepack_weight (debug/verification):
+ * writes wq[n, k] for n < N, k < K; other bytes of wq are not touched.
+ */
+w8a8_status_t int8_unpack_weight(const void *w_packed, int64_t N, int64_t K, int8_t *wq,
+                                 int64_t ldw, void *stream);
+
+/*
+ * int8_scaled_mm - int8 x int8 -> int32 matmul with the scale epilogue
+ * (page "Issue 5 probe ...", "Round two" kernel-path paragraph: the scaled
+ * matmul after the per-token quant, whose reference must include the
+ * act_scale factor; page "INT8 Quant for Dual-Max Recipe": W8A8 runs
+ * int8 x int8 with no dequantization).
+ *
+ *   acc[m,n] = sum_{k<K} xq[m,k] * wq[n,k]                (exact, int32)
+ *   W8A8_OUT_BF16: out[m,n] = bf16_rne( fl32(fl32(fl32(acc) * x_scale[m]) * w_scale[n])
+ *                                        [+ bias[n], rounded to fp32] )
+ *   W8A8_OUT_I32:  out[m,n] = acc[m,n]
+ * Inputs: xq int8 [M, ldq]; x_scale fp32 [M]; w_packed from
+ * int8_prepack_weight(N, K); w_scale fp32 [N]; bias bf16 [N] or NULL.
+ * Output: bf16 or int32 [M, ldo].
+ * Requirements: M >= 0 (M == 0 is a no-op), N >= 1, 16 <= K <= W8A8_MAX_K
+ * with K a multiple of 16, ldq >= K, ldo >= N; xq and w_packed 16-byte
+ * aligned, ldq a multiple of 16; out aligned to its element size. In I32
+ * mode x_scale, w_scale and bias may be NULL and are ignored.
+ */
+w8a8_status_t int8_scaled_mm(const int8_t *xq, int64_t ldq, const float *x_scale,
+                             const void *w_packed, const float *w_scale, const uint16_t *bias,
+                             int64_t M, int64_t N, int64_t K, int mode, void *out, int64_t ldo,
+                             void *stream);
+
+/*
+ * int8_scaled_mm_tile - int8_scaled_mm with an explicit tile configuration
+ * (0 <= tile < w8a8_mm_tile_count()), or -1 for the automatic choice that
+ * int8_scaled_mm makes. Every tile computes bit-identical results; this
+ * exists for tuning and for testing each configuration.
+ */
+w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const float *x_scale,
+                                  const void *w_packed, const float *w_scale,
+                                  const uint16_t *bias, int64_t M, int64_t N, int64_t K, int mode,
+                                  void *out, int64_t ldo, void *stream, int tile);
+
+/* Number of tile configurations, a short name of one ("128x128x128/2x2"),
+ * and the tile the automatic choice picks for a shape. */
+int w8a8_mm_tile_count(void);
+const char *w8a8_mm_tile_name(int tile);
+int w8a8_mm_tile_auto(int64_t M, int64_t N, int64_t K);
+
+/* 1 when `device` is a gfx950 GPU this library can run on, else 0. */
+int w8a8_device_supported(int device);
+
+/* Static description of a status code. */
+const char *w8a8_status_string(int status);
+
+/* Thread-local detail of the most recent error returned on this thread
+ * (argument name, HIP error string); "" when there is none. */
+const char *w8a8_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

@@ -1,0 +1,185 @@
+"""libw8a8 C ABI on the CPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call.
+
+No call here launches a kernel: argument errors return before the device is
+touched, and on a machine without a GPU a well-formed call must fail with
+W8A8_ERR_DEVICE (never a silent fallback).
+"""
+import ast
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w8a8.h")
+PKG = os.path.join(ROOT, "w8a8_int8_dynamic_amd")
+
+from w8a8_int8_dynamic_amd import _lib  # noqa: E402
+
+L = _lib.lib()
+OK, NULL, SHAPE, ALIGN, DEVICE, MODE = 0, 1, 2, 3, 4, 5
+A = 0x10000          # a 16-byte-aligned fake device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(\w+)\s*\(", text, flags=re.M)) -
+                  {"defined"})
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for must in ("int8_prepack_weight", "int8_quant_per_token", "int8_scaled_mm",
+                 "int8_quant_per_channel", "int8_unpack_weight", "int8_prepack_weight_bytes"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    exported = subprocess.run(["nm", "-D", "--defined-only", _lib.LIBRARY], capture_output=True,
+                              text=True, check=True).stdout
+    syms = {line.split()[-1] for line in exported.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in syms, f"{name} declared in w8a8.h but not exported"
+        assert hasattr(L, name)
+    # the binding's signature table covers exactly the header
+    assert sorted(_lib.SIGNATURES) == declared_functions()
+
+
+def test_only_the_abi_is_exported():
+    exported = subprocess.run(["nm", "-D", "--defined-only", _lib.LIBRARY], capture_output=True,
+                              text=True, check=True).stdout
+    text_syms = {line.split()[-1] for line in exported.splitlines()
+                 if len(line.split()) == 3 and line.split()[1] == "T"}
+    assert text_syms <= set(declared_functions()), text_syms - set(declared_functions())
+
+
+def test_constants_match_header():
+    text = open(HEADER).read()
+    assert f"#define W8A8_MAX_K {_lib.W8A8_MAX_K}" in text
+    assert 128 * 128 * _lib.W8A8_MAX_K < 2 ** 31 and _lib.W8A8_MAX_K % 16 == 0
+    assert 128 * 128 * (_lib.W8A8_MAX_K + 16) >= 2 ** 31
+
+
+def test_status_strings():
+    for s in range(7):
+        assert _lib.status_string(s) and _lib.status_string(s) != "unknown status"
+    assert _lib.status_string(99) == "unknown status"
+
+
+def test_prepack_bytes():
+    f = L.int8_prepack_weight_bytes
+    assert f(1, 1) == 16 * 64
+    assert f(16, 64) == 1024
+    assert f(17, 65) == 32 * 128
+    assert f(12288, 4096) == 12288 * 4096
+    assert f(0, 64) == 0 and f(16, 0) == 0 and f(-1, 64) == 0
+    assert f(2 ** 31, 64) == 0
+
+
+def quant(x=A, M=4, K=64, ldx=64, q=A, ldq=64, s=A):
+    return L.int8_quant_per_token(x, M, K, ldx, q, ldq, s, None)
+
+
+def qchan(w=A, N=4, K=64, ldw=64, q=A, ldq=64, s=A):
+    return L.int8_quant_per_channel(w, N, K, ldw, q, ldq, s, None)
+
+
+def test_quant_validation():
+    assert quant(M=-1) == SHAPE
+    assert quant(K=0) == SHAPE
+    assert quant(ldx=63) == SHAPE
+    assert quant(ldq=63) == SHAPE
+    assert quant(M=0, x=None, q=None, s=None) == OK          # empty is a no-op
+    assert quant(x=None) == NULL and quant(q=None) == NULL and quant(s=None) == NULL
+    assert quant(x=A + 8) == ALIGN                           # bf16 rows need 16 bytes
+    assert quant(ldx=68, K=64) == ALIGN                      # ldx % 8
+    assert quant(q=A + 4) == ALIGN and quant(ldq=68) == ALIGN
+    assert quant(s=A + 2) == ALIGN
+    assert qchan(ldw=66) == ALIGN                            # fp32 rows: ldw % 4
+    assert qchan(ldw=68) in (OK, DEVICE)
+    assert "int8_quant_per_token" in (quant(x=None) and _lib.last_error())
+
+
+def test_prepack_validation():
+    p = L.int8_prepack_weight
+    assert p(A, 0, 64, 64, A, None) == SHAPE
+    assert p(A, 16, 0, 64, A, None) == SHAPE
+    assert p(A, 16, 64, 63, A, None) == SHAPE
+    assert p(None, 16, 64, 64, A, None) == NULL
+    assert p(A, 16, 64, 64, None, None) == NULL
+    assert p(A, 16, 64, 64, A + 8, None) == ALIGN
+    u = L.int8_unpack_weight
+    assert u(A + 8, 16, 64, A, 64, None) == ALIGN
+    assert u(A, 16, 64, None, 64, None) == NULL
+
+
+def mm(xq=A, ldq=64, xs=A, wp=A, ws=A, bias=None, M=4, N=16, K=64, mode=0, out=A, ldo=16, tile=-1):
+    return L.int8_scaled_mm_tile(xq, ldq, xs, wp, ws, bias, M, N, K, mode, out, ldo, None, tile)
+
+
+def test_scaled_mm_validation():
+    assert mm(mode=2) == MODE and mm(mode=-1) == MODE
+    assert mm(tile=L.w8a8_mm_tile_count()) == MODE and mm(tile=-2) == MODE
+    assert mm(M=-1) == SHAPE and mm(N=0) == SHAPE
+    assert mm(K=0) == SHAPE and mm(K=8) == SHAPE and mm(K=72) == SHAPE
+    assert mm(K=_lib.W8A8_MAX_K + 16, ldq=_lib.W8A8_MAX_K + 16) == SHAPE
+    assert mm(ldq=48) == SHAPE and mm(ldo=15) == SHAPE
+    assert mm(M=0, xq=None, xs=None, wp=None, ws=None, out=None) == OK
+    assert mm(xq=None) == NULL and mm(wp=None) == NULL and mm(out=None) == NULL
+    assert mm(xs=None) == NULL and mm(ws=None) == NULL
+    assert mm(xq=A + 8) == ALIGN and mm(ldq=72, K=64) == ALIGN and mm(wp=A + 4) == ALIGN
+    assert mm(out=A + 1) == ALIGN and mm(out=A + 2, mode=1) == ALIGN
+    assert mm(xs=A + 2) == ALIGN and mm(bias=A + 1) == ALIGN
+    # int32 debug mode ignores scales and bias
+    assert mm(mode=1, xs=None, ws=None, bias=A + 1) in (OK, DEVICE)
+
+
+def test_no_fallback_without_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert quant() == DEVICE
+    assert mm() == DEVICE
+    assert L.int8_prepack_weight(A, 16, 64, 64, A, None) == DEVICE
+    assert L.w8a8_device_supported(0) == 0
+    assert "device" in _lib.last_error()
+
+
+def test_tile_table():
+    n = L.w8a8_mm_tile_count()
+    assert n >= 4
+    names = [L.w8a8_mm_tile_name(i).decode() for i in range(n)]
+    assert len(set(names)) == n and all(names)
+    assert L.w8a8_mm_tile_name(n) == b""
+    for shape in [(512, 12288, 4096), (512, 4096, 4096), (4096, 12288, 3072),
+                  (8192, 3072, 12288), (64, 128, 256), (1, 1, 16)]:
+        t = L.w8a8_mm_tile_auto(*shape)
+        assert 0 <= t < n
+        assert t == L.w8a8_mm_tile_auto(*shape)             # deterministic
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    from w8a8_int8_dynamic_amd import ops
+    with pytest.raises(ValueError):
+        ops.quant_per_token(torch.zeros(4, 64, dtype=torch.bfloat16))
+
+
+def test_product_never_touches_the_oracle():
+    """No module of the package imports or loads the oracle."""
+    for dirpath, _, files in os.walk(PKG):
+        for f in files:
+            path = os.path.join(dirpath, f)
+            if f.endswith(".py"):
+                tree = ast.parse(open(path).read())
+                for node in ast.walk(tree):
+                    if isinstance(node, ast.Import):
+                        assert not any(a.name.split(".")[0] == "oracle" for a in node.names), path
+                    if isinstance(node, ast.ImportFrom):
+                        assert (node.module or "").split(".")[0] != "oracle", path
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                assert "liboracle" not in open(path).read(), path

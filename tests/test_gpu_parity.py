@@ -1,0 +1,324 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: int8 codes, fp32 scales, prepacked bytes and int32 accumulators are
+bit-exact; bf16 outputs satisfy |g - r| <= 1e-2*|r| + 1e-4*rms(r[m,:])
+against the oracle's fp64 epilogue, and are expected to equal the oracle's
+fixed-order fp32 epilogue bit for bit.
+
+Sizes: small and mid shapes span several tiles with ragged M/N/K tails and
+run the oracle in full; the five workload shapes run at full size in the
+launch configuration the benchmark times, checked on sampled token rows
+(oracle row by row) plus exact int64 row- and column-sum identities of the
+accumulators over every row and column.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+RTOL, ATOL_RMS = 1e-2, 1e-4
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from w8a8_int8_dynamic_amd import ops as _ops
+    assert _ops.device_supported(torch.cuda.current_device()), "not a gfx950 device"
+    return _ops
+
+
+DEV = "cuda"
+
+
+def bf16_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def bits_np(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def f64(bits: np.ndarray) -> np.ndarray:
+    return wl.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def check_out(got: np.ndarray, ref32: np.ndarray, ref64: np.ndarray, what: str) -> float:
+    """Tolerance bar against the fp64 epilogue; returns the bit-exact fraction vs fp32."""
+    g, r = f64(got), f64(ref64)
+    assert np.all(np.isfinite(g)), what
+    rms = np.sqrt(np.mean(r * r, axis=1, keepdims=True))
+    bad = np.abs(g - r) > RTOL * np.abs(r) + ATOL_RMS * rms
+    assert not bad.any(), f"{what}: {bad.sum()} outputs outside tolerance"
+    return float(np.mean(got == ref32))
+
+
+def rand_i8(rng, shape, lo=-127):
+    return rng.integers(lo, 128, shape, dtype=np.int8)
+
+
+# ---------------------------------------------------------------------------
+# Quantization
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", [w.name for w in wl.WORKLOADS])
+def test_quant_per_token_workload(ops, orc, name):
+    inp = wl.generate(wl.by_name(name))
+    xq, xs = ops.quant_per_token(bf16_dev(inp.x_bf16))
+    q_ref, s_ref = orc.quant_per_token(inp.x_bf16)
+    assert np.array_equal(xs.cpu().numpy(), s_ref)
+    assert np.array_equal(xq.cpu().numpy(), q_ref)
+
+
+@pytest.mark.parametrize("name", [w.name for w in wl.WORKLOADS])
+def test_quant_per_channel_workload(ops, orc, name):
+    inp = wl.generate(wl.by_name(name))
+    wq, ws = ops.quant_per_channel(torch.from_numpy(inp.w_f32).to(DEV))
+    q_ref, s_ref = orc.quant_per_channel(inp.w_f32)
+    assert np.array_equal(ws.cpu().numpy(), s_ref)
+    assert np.array_equal(wq.cpu().numpy(), q_ref)
+
+
+def _edge_rows(rng, M, K):
+    x = (rng.standard_normal((M, K)) * 10.0 ** rng.uniform(-3, 3, (M, 1))).astype(np.float32)
+    if M > 4:
+        x[1] = 0.0                                   # all-zero row
+        x[2] = 0.0
+        x[2, K // 2] = 2.0 ** -101                   # below the zero-row threshold
+        x[3] = np.round(x[3])                        # integers: many exact ties below
+        x[3, 0] = 127.0 * np.sign(x[3, 0] or 1.0)
+        x[3, 1:] = np.clip(x[3, 1:], -126, 126) + 0.5
+    return x
+
+
+@pytest.mark.parametrize("M,K,pad", [(1, 1, 0), (3, 3, 8), (5, 8, 0), (7, 9, 0), (33, 100, 8),
+                                     (64, 511, 0), (130, 513, 16), (9, 4097, 0), (600, 4096, 0),
+                                     (17, 12288, 0), (5, 20000, 8), (3, 40000, 0)])
+def test_quant_per_token_edges(ops, orc, M, K, pad):
+    rng = np.random.default_rng(1000 + M + K)
+    bits = wl.f32_to_bf16_bits(_edge_rows(rng, M, K))
+    ldx = -(-K // 8) * 8 + pad
+    xpad = np.zeros((M, ldx), np.uint16)
+    xpad[:, :K] = bits
+    xpad[:, K:] = 0x4780                             # large values beyond K must be ignored
+    ldq = -(-K // 8) * 8 + 8
+    x_d = bf16_dev(xpad)
+    xq = torch.full((M, ldq), 0x5A, dtype=torch.int8, device=DEV)
+    xs = torch.empty(M, dtype=torch.float32, device=DEV)
+    ops.quant_per_token(x_d[:, :K], xq[:, :K], xs)
+    q_ref, s_ref = orc.quant_per_token(bits)
+    got = xq.cpu().numpy()
+    assert np.array_equal(xs.cpu().numpy(), s_ref)
+    assert np.array_equal(got[:, :K], q_ref)
+    assert np.all(got[:, K:] == 0x5A), "wrote past K"
+
+
+@pytest.mark.parametrize("N,K", [(1, 1), (3, 5), (17, 64), (40, 1000), (2, 40000)])
+def test_quant_per_channel_edges(ops, orc, N, K):
+    rng = np.random.default_rng(2000 + N + K)
+    w = _edge_rows(rng, N, K)
+    wq, ws = ops.quant_per_channel(torch.from_numpy(w).to(DEV))
+    q_ref, s_ref = orc.quant_per_channel(w)
+    assert np.array_equal(ws.cpu().numpy(), s_ref)
+    assert np.array_equal(wq.cpu().numpy(), q_ref)
+
+
+def test_quant_empty(ops):
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    xq, xs = ops.quant_per_token(x)
+    assert xq.shape == (0, 64) and xs.shape == (0,)
+
+
+# ---------------------------------------------------------------------------
+# Prepack
+# ---------------------------------------------------------------------------
+def packed_reference(wq: np.ndarray) -> np.ndarray:
+    """The byte layout stated in include/w8a8.h, built with NumPy indexing."""
+    N, K = wq.shape
+    Np, Kp = -(-N // 16) * 16, -(-K // 64) * 64
+    w = np.zeros((Np, Kp), np.int8)
+    w[:N, :K] = wq
+    # F[nb][kb] byte 16*l + j = w[16*nb + l%16, 64*kb + 16*(l//16) + j]
+    f = w.reshape(Np // 16, 16, Kp // 64, 4, 16)          # nb, l%16, kb, l//16, j
+    f = f.transpose(0, 2, 3, 1, 4)                        # nb, kb, l//16, l%16, j
+    return np.ascontiguousarray(f).reshape(-1).view(np.uint8)
+
+
+@pytest.mark.parametrize("N,K", [(1, 1), (17, 65), (40, 200), (256, 4096), (3072, 12288)])
+def test_prepack_layout_and_roundtrip(ops, N, K):
+    rng = np.random.default_rng(3000 + N)
+    wq = rand_i8(rng, (N, K), lo=-128)
+    w_d = torch.from_numpy(wq).to(DEV)
+    packed = ops.prepack_weight(w_d)
+    assert np.array_equal(packed.cpu().numpy(), packed_reference(wq))
+    assert np.array_equal(ops.unpack_weight(packed, N, K).cpu().numpy(), wq)
+
+
+# ---------------------------------------------------------------------------
+# Scaled matmul on small and mid shapes, every tile configuration
+# ---------------------------------------------------------------------------
+SHAPES = [(1, 1, 16), (37, 45, 80), (130, 200, 336), (257, 300, 1040), (64, 128, 256),
+          (300, 520, 576)]
+
+
+def _mm_case(seed, M, N, K, bias=True):
+    inp = wl.random_case(M, K, N, seed, bias=bias)
+    return inp
+
+
+def _ntiles(ops):
+    return list(range(ops.tile_count()))
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_scaled_mm_i32_every_tile(ops, orc, M, N, K):
+    rng = np.random.default_rng(4000 + M + N + K)
+    xq = rand_i8(rng, (M, K), lo=-128)
+    wq = rand_i8(rng, (N, K), lo=-128)
+    ref = orc.gemm_i32(xq, wq)
+    xq_d = torch.from_numpy(xq).to(DEV)
+    packed = ops.prepack_weight(torch.from_numpy(wq).to(DEV))
+    for t in _ntiles(ops):
+        acc = ops.scaled_mm(xq_d, None, packed, None, N, out_dtype=torch.int32, tile=t)
+        assert np.array_equal(acc.cpu().numpy(), ref), f"tile {ops.tile_name(t)}"
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("bias", [False, True])
+def test_scaled_mm_bf16_every_tile(ops, orc, M, N, K, bias):
+    inp = _mm_case(5000 + M + N + K, M, N, K, bias)
+    wq, ws = orc.quant_per_channel(inp.w_f32)
+    xq, xs = orc.quant_per_token(inp.x_bf16)
+    acc = orc.gemm_i32(xq, wq)
+    ref32 = orc.epilogue_f32(acc, xs, ws, inp.bias_bf16)
+    ref64 = orc.epilogue_f64(acc, xs, ws, inp.bias_bf16)
+    xq_d, xs_d = torch.from_numpy(xq).to(DEV), torch.from_numpy(xs).to(DEV)
+    ws_d = torch.from_numpy(ws).to(DEV)
+    b_d = None if inp.bias_bf16 is None else bf16_dev(inp.bias_bf16)
+    packed = ops.prepack_weight(torch.from_numpy(wq).to(DEV))
+    for t in _ntiles(ops):
+        out = ops.scaled_mm(xq_d, xs_d, packed, ws_d, N, b_d, tile=t)
+        got = bits_np(out)
+        exact = check_out(got, ref32, ref64, f"tile {ops.tile_name(t)}")
+        assert exact == 1.0, f"tile {ops.tile_name(t)}: {exact:.6f} bit-exact vs fp32 epilogue"
+
+
+def test_scaled_mm_strided_output_and_unaligned_rows(ops, orc):
+    """Leading dimensions larger than the row, odd ldo (scalar store path)."""
+    M, N, K = 70, 37, 96
+    inp = _mm_case(6001, M, N, K)
+    wq, ws = orc.quant_per_channel(inp.w_f32)
+    xq, xs = orc.quant_per_token(inp.x_bf16)
+    acc = orc.gemm_i32(xq, wq)
+    ref32 = orc.epilogue_f32(acc, xs, ws, inp.bias_bf16)
+    xq_big = torch.zeros((M, K + 32), dtype=torch.int8, device=DEV)
+    xq_big[:, :K] = torch.from_numpy(xq).to(DEV)
+    packed = ops.prepack_weight(torch.from_numpy(wq).to(DEV))
+    for ldo in (N, N + 3, 64):
+        out_big = torch.full((M, ldo), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+        ops.scaled_mm(xq_big[:, :K], torch.from_numpy(xs).to(DEV), packed,
+                      torch.from_numpy(ws).to(DEV), N, bf16_dev(inp.bias_bf16), out=out_big[:, :N])
+        got = bits_np(out_big)
+        assert np.array_equal(got[:, :N], ref32)
+        assert np.all(got[:, N:] == 0xFFFF), "wrote past N"
+
+
+def test_scaled_mm_empty_and_determinism(ops, orc):
+    packed = ops.prepack_weight(torch.zeros((16, 64), dtype=torch.int8, device=DEV))
+    out = ops.scaled_mm(torch.empty((0, 64), dtype=torch.int8, device=DEV),
+                        torch.empty(0, device=DEV), packed, torch.ones(16, device=DEV), 16)
+    assert out.shape == (0, 16)
+    M, N, K = 300, 520, 576
+    inp = _mm_case(6002, M, N, K)
+    wq, ws = orc.quant_per_channel(inp.w_f32)
+    x_d = bf16_dev(inp.x_bf16)
+    xq, xs = ops.quant_per_token(x_d)
+    packed = ops.prepack_weight(torch.from_numpy(wq).to(DEV))
+    ws_d, b_d = torch.from_numpy(ws).to(DEV), bf16_dev(inp.bias_bf16)
+    first = ops.scaled_mm(xq, xs, packed, ws_d, N, b_d)
+    for _ in range(50):
+        again = ops.scaled_mm(xq, xs, packed, ws_d, N, b_d)
+        assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        other = ops.scaled_mm(xq, xs, packed, ws_d, N, b_d)
+    s.synchronize()
+    assert torch.equal(first.view(torch.int16), other.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at full size, in the benchmark's launch configuration
+# ---------------------------------------------------------------------------
+def _sample_rows(M, rng, n=40):
+    rows = set(rng.choice(M, min(M, n), replace=False).tolist())
+    rows |= {0, M - 1, (M - 1) // 2}
+    return np.array(sorted(rows), np.int64)
+
+
+@pytest.mark.parametrize("name", [w.name for w in wl.WORKLOADS])
+def test_workload_full_size(ops, orc, name):
+    w = wl.by_name(name)
+    inp = wl.generate(w)
+    from w8a8_int8_dynamic_amd import W8A8Linear
+    layer = W8A8Linear.from_float(torch.from_numpy(inp.w_f32).to(DEV),
+                                  None if inp.bias_bf16 is None else bf16_dev(inp.bias_bf16))
+    x_d = bf16_dev(inp.x_bf16)
+    out = layer(x_d)
+    torch.cuda.synchronize()
+    assert out.shape == (w.M, w.N) and out.dtype == torch.bfloat16
+    # operands, bit-exact
+    wq_ref, ws_ref = orc.quant_per_channel(inp.w_f32)
+    assert np.array_equal(layer.w_scale.cpu().numpy(), ws_ref)
+    assert np.array_equal(ops.unpack_weight(layer.w_packed, w.N, w.K).cpu().numpy(), wq_ref)
+    xq, xs = ops.quant_per_token(x_d)
+    xq_ref, xs_ref = orc.quant_per_token(inp.x_bf16)
+    assert np.array_equal(xq.cpu().numpy(), xq_ref) and np.array_equal(xs.cpu().numpy(), xs_ref)
+    # accumulators: sampled rows exactly, and exact row/column sums of every row and column
+    acc = ops.scaled_mm(xq, None, layer.w_packed, None, w.N, out_dtype=torch.int32).cpu().numpy()
+    rows = _sample_rows(w.M, np.random.default_rng(w.seed))
+    acc_ref = orc.gemm_i32(xq_ref, wq_ref, rows)
+    assert np.array_equal(acc[rows], acc_ref)
+    xq64, wq64 = xq_ref.astype(np.int64), wq_ref.astype(np.int64)
+    assert np.array_equal(acc.sum(axis=1, dtype=np.int64), xq64 @ wq64.sum(axis=0))
+    assert np.array_equal(acc.sum(axis=0, dtype=np.int64), xq64.sum(axis=0) @ wq64.T)
+    # outputs on the sampled rows
+    got = bits_np(out)[rows]
+    ref32 = orc.epilogue_f32(acc_ref, xs_ref[rows], ws_ref, inp.bias_bf16)
+    ref64 = orc.epilogue_f64(acc_ref, xs_ref[rows], ws_ref, inp.bias_bf16)
+    exact = check_out(got, ref32, ref64, name)
+    assert exact == 1.0, f"{name}: {exact:.6f} bit-exact"
+    # every output finite; bf16 rounding vs fp64 on the dequantized operands ~0.17 %
+    assert torch.isfinite(out.float()).all()
+    deq = (xq_ref[rows].astype(np.float64) * xs_ref[rows, None].astype(np.float64)) @ \
+          (wq_ref.astype(np.float64) * ws_ref[:, None].astype(np.float64)).T
+    if inp.bias_bf16 is not None:
+        deq += f64(inp.bias_bf16)[None, :]
+    rel = np.linalg.norm(f64(got) - deq) / np.linalg.norm(deq)
+    print(f"\n{name}: rel-L2 vs fp64 dequantized reference {100 * rel:.4f} %")
+    assert rel < 0.0025
+
+
+def test_linear_keeps_leading_dims(ops, orc):
+    from w8a8_int8_dynamic_amd import W8A8Linear
+    inp = wl.random_case(2 * 37, 320, 48, 7001)
+    layer = W8A8Linear.from_float(torch.from_numpy(inp.w_f32).to(DEV), bf16_dev(inp.bias_bf16))
+    x = bf16_dev(inp.x_bf16)
+    y2 = layer(x)
+    y3 = layer(x.view(2, 37, 320))
+    assert y3.shape == (2, 37, 48)
+    assert torch.equal(y3.reshape(74, 48).view(torch.int16), y2.view(torch.int16))
+    with pytest.raises(ValueError):
+        layer(x[:, :300])
+
+
+def test_binding_errors_on_device(ops):
+    from w8a8_int8_dynamic_amd import W8A8Error
+    xq = torch.zeros((4, 72), dtype=torch.int8, device=DEV)
+    packed = ops.prepack_weight(torch.zeros((16, 72), dtype=torch.int8, device=DEV))
+    with pytest.raises(W8A8Error) as e:
+        ops.scaled_mm(xq, torch.ones(4, device=DEV), packed, torch.ones(16, device=DEV), 16)
+    assert e.value.status == 2    # K = 72 is not a multiple of 16

@@ -1,0 +1,264 @@
+// C ABI of libw8a8 (declared in include/w8a8.h): argument checks, device
+// check, and dispatch to the HIP kernels. Every check that can be made on
+// the host runs before the first HIP call, so a bad argument never reaches
+// the device and can be tested without one.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <string>
+
+#include "../../include/w8a8.h"
+#include "internal.hpp"
+
+#define W8A8_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+w8a8_status_t fail(w8a8_status_t s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+w8a8_status_t fail(w8a8_status_t s, const char *fmt, ...)
+{
+    char buf[256];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+w8a8_status_t ok()
+{
+    g_last_error.clear();
+    return W8A8_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxRows = std::numeric_limits<int32_t>::max();
+
+// Per-device cache of "is gfx950": 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_ok[kMaxDevices];
+
+int query_supported(int device)
+{
+    if (device < 0 || device >= kMaxDevices)
+        return 0;
+    int c = g_dev_ok[device].load(std::memory_order_relaxed);
+    if (c == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, device) != hipSuccess)
+            return 0;   // not cached: the device may become usable later
+        c = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_dev_ok[device].store(c, std::memory_order_relaxed);
+    }
+    return c == 1;
+}
+
+w8a8_status_t check_device()
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(W8A8_ERR_DEVICE, "no current HIP device: %s", hipGetErrorString(e));
+    if (!query_supported(dev))
+        return fail(W8A8_ERR_DEVICE, "device %d is not a gfx950 GPU", dev);
+    return W8A8_OK;
+}
+
+w8a8_status_t launched(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(W8A8_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+w8a8_status_t quant_common(const void *x, bool f32, int64_t M, int64_t K, int64_t ldx, int8_t *q,
+                           int64_t ldq, float *s, void *stream, const char *what)
+{
+    if (M < 0 || M > kMaxRows)
+        return fail(W8A8_ERR_SHAPE, "%s: rows %lld out of range", what, (long long)M);
+    if (K < 1 || K > kMaxRows)
+        return fail(W8A8_ERR_SHAPE, "%s: K %lld out of range", what, (long long)K);
+    if (ldx < K || ldq < K)
+        return fail(W8A8_ERR_SHAPE, "%s: leading dimension smaller than K", what);
+    if (M == 0)
+        return ok();
+    if (!x || !q || !s)
+        return fail(W8A8_ERR_NULL, "%s: NULL tensor pointer", what);
+    const int64_t vec = f32 ? 4 : 8;
+    if (!aligned(x, 16) || ldx % vec != 0)
+        return fail(W8A8_ERR_ALIGN, "%s: input must be 16-byte aligned with ld a multiple of %lld",
+                    what, (long long)vec);
+    if (!aligned(q, 8) || ldq % 8 != 0)
+        return fail(W8A8_ERR_ALIGN, "%s: codes must be 8-byte aligned with ld a multiple of 8", what);
+    if (!aligned(s, 4))
+        return fail(W8A8_ERR_ALIGN, "%s: scales must be 4-byte aligned", what);
+    w8a8_status_t st = check_device();
+    if (st != W8A8_OK)
+        return st;
+    return launched(w8a8::launch_quant_rows(x, f32, M, K, ldx, q, ldq, s,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                    what);
+}
+
+w8a8_status_t pack_common(int64_t N, int64_t K, int64_t ldw, const void *a, const void *b,
+                          const void *packed, const char *what)
+{
+    if (N < 1 || N > kMaxRows || K < 1 || K > kMaxRows)
+        return fail(W8A8_ERR_SHAPE, "%s: N and K must be in [1, 2^31)", what);
+    if (ldw < K)
+        return fail(W8A8_ERR_SHAPE, "%s: ldw smaller than K", what);
+    if (int8_prepack_weight_bytes(N, K) == 0)
+        return fail(W8A8_ERR_SHAPE, "%s: packed size overflows", what);
+    if (!a || !b)
+        return fail(W8A8_ERR_NULL, "%s: NULL tensor pointer", what);
+    if (!aligned(packed, 16))
+        return fail(W8A8_ERR_ALIGN, "%s: packed weight must be 16-byte aligned", what);
+    return check_device();
+}
+
+}  // namespace
+
+W8A8_API w8a8_status_t int8_quant_per_token(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                                            int8_t *xq, int64_t ldq, float *x_scale, void *stream)
+{
+    return quant_common(x, false, M, K, ldx, xq, ldq, x_scale, stream, "int8_quant_per_token");
+}
+
+W8A8_API w8a8_status_t int8_quant_per_channel(const float *w, int64_t N, int64_t K, int64_t ldw,
+                                              int8_t *wq, int64_t ldq, float *w_scale,
+                                              void *stream)
+{
+    return quant_common(w, true, N, K, ldw, wq, ldq, w_scale, stream, "int8_quant_per_channel");
+}
+
+W8A8_API size_t int8_prepack_weight_bytes(int64_t N, int64_t K)
+{
+    if (N < 1 || K < 1 || N > kMaxRows || K > kMaxRows)
+        return 0;
+    const unsigned __int128 n = (unsigned __int128)w8a8::round_up(N, w8a8::kFragN);
+    const unsigned __int128 k = (unsigned __int128)w8a8::round_up(K, w8a8::kFragK);
+    const unsigned __int128 bytes = n * k;
+    if (bytes > (unsigned __int128)std::numeric_limits<size_t>::max() / 2)
+        return 0;
+    return (size_t)bytes;
+}
+
+W8A8_API w8a8_status_t int8_prepack_weight(const int8_t *wq, int64_t N, int64_t K, int64_t ldw,
+                                           void *w_packed, void *stream)
+{
+    w8a8_status_t st = pack_common(N, K, ldw, wq, w_packed, w_packed, "int8_prepack_weight");
+    if (st != W8A8_OK)
+        return st;
+    return launched(w8a8::launch_prepack(wq, N, K, ldw, w_packed,
+                                         reinterpret_cast<hipStream_t>(stream)),
+                    "int8_prepack_weight");
+}
+
+W8A8_API w8a8_status_t int8_unpack_weight(const void *w_packed, int64_t N, int64_t K, int8_t *wq,
+                                          int64_t ldw, void *stream)
+{
+    w8a8_status_t st = pack_common(N, K, ldw, w_packed, wq, w_packed, "int8_unpack_weight");
+    if (st != W8A8_OK)
+        return st;
+    return launched(w8a8::launch_unpack(w_packed, N, K, wq, ldw,
+                                        reinterpret_cast<hipStream_t>(stream)),
+                    "int8_unpack_weight");
+}
+
+W8A8_API w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const float *x_scale,
+                                           const void *w_packed, const float *w_scale,
+                                           const uint16_t *bias, int64_t M, int64_t N, int64_t K,
+                                           int mode, void *out, int64_t ldo, void *stream,
+                                           int tile)
+{
+    const char *what = "int8_scaled_mm";
+    if (mode != W8A8_OUT_BF16 && mode != W8A8_OUT_I32)
+        return fail(W8A8_ERR_MODE, "%s: unknown output mode %d", what, mode);
+    if (tile < -1 || tile >= w8a8::mm_tile_count())
+        return fail(W8A8_ERR_MODE, "%s: unknown tile %d", what, tile);
+    if (M < 0 || M > kMaxRows || N < 1 || N > kMaxRows)
+        return fail(W8A8_ERR_SHAPE, "%s: M or N out of range", what);
+    if (K < 16 || K > W8A8_MAX_K || K % 16 != 0)
+        return fail(W8A8_ERR_SHAPE, "%s: K must be a multiple of 16 in [16, %d]", what, W8A8_MAX_K);
+    if (ldq < K || ldo < N)
+        return fail(W8A8_ERR_SHAPE, "%s: leading dimension too small", what);
+    if (M == 0)
+        return ok();
+    const bool i32 = mode == W8A8_OUT_I32;
+    if (!xq || !w_packed || !out || (!i32 && (!x_scale || !w_scale)))
+        return fail(W8A8_ERR_NULL, "%s: NULL tensor pointer", what);
+    if (!aligned(xq, 16) || ldq % 16 != 0 || !aligned(w_packed, 16))
+        return fail(W8A8_ERR_ALIGN, "%s: xq/w_packed must be 16-byte aligned, ldq a multiple of 16",
+                    what);
+    const uintptr_t esz = i32 ? 4 : 2;
+    if (!aligned(out, esz))
+        return fail(W8A8_ERR_ALIGN, "%s: out must be aligned to its element size", what);
+    if (!i32 && (!aligned(x_scale, 4) || !aligned(w_scale, 4) || (bias && !aligned(bias, 2))))
+        return fail(W8A8_ERR_ALIGN, "%s: scales/bias misaligned", what);
+    const int t = tile >= 0 ? tile : w8a8::mm_tile_auto(M, N, K);
+    w8a8_status_t st = check_device();
+    if (st != W8A8_OK)
+        return st;
+
+    w8a8::MmArgs a;
+    a.xq = xq;
+    a.xs = i32 ? nullptr : x_scale;
+    a.wp = reinterpret_cast<const int8_t *>(w_packed);
+    a.ws = i32 ? nullptr : w_scale;
+    a.bias = i32 ? nullptr : bias;
+    a.out = out;
+    a.ldq = ldq;
+    a.ldo = ldo;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.kblocks = (int)w8a8::ceil_div(K, w8a8::kFragK);
+    a.nblocks = (int)w8a8::ceil_div(N, w8a8::kFragN);
+    // 8-byte bf16 / 16-byte int32 stores of 4 consecutive channels need every
+    // row start (and channel multiples of 4) aligned to that width.
+    const uintptr_t vw = 4 * esz;
+    a.vec_store = aligned(out, vw) && ((uint64_t)ldo * esz) % vw == 0;
+    return launched(w8a8::launch_scaled_mm(a, i32, t, reinterpret_cast<hipStream_t>(stream)), what);
+}
+
+W8A8_API w8a8_status_t int8_scaled_mm(const int8_t *xq, int64_t ldq, const float *x_scale,
+                                      const void *w_packed, const float *w_scale,
+                                      const uint16_t *bias, int64_t M, int64_t N, int64_t K,
+                                      int mode, void *out, int64_t ldo, void *stream)
+{
+    return int8_scaled_mm_tile(xq, ldq, x_scale, w_packed, w_scale, bias, M, N, K, mode, out, ldo,
+                               stream, -1);
+}
+
+W8A8_API int w8a8_mm_tile_count(void) { return w8a8::mm_tile_count(); }
+
+W8A8_API const char *w8a8_mm_tile_name(int tile) { return w8a8::mm_tile_name(tile); }
+
+W8A8_API int w8a8_mm_tile_auto(int64_t M, int64_t N, int64_t K)
+{
+    return w8a8::mm_tile_auto(M, N, K);
+}
+
+W8A8_API int w8a8_device_supported(int device) { return query_supported(device); }
+
+W8A8_API const char *w8a8_status_string(int status)
+{
+    switch (status) {
+    case W8A8_OK: return "success";
+    case W8A8_ERR_NULL: return "a required pointer is NULL";
+    case W8A8_ERR_SHAPE: return "a size or leading dimension is out of range";
+    case W8A8_ERR_ALIGN: return "a pointer or leading dimension breaks an alignment rule";
+    case W8A8_ERR_DEVICE: return "no usable current device, or it is not gfx950";
+    case W8A8_ERR_MODE: return "unknown output mode or tile id";
+    case W8A8_ERR_HIP: return "the HIP runtime reported an error when launching";
+    default: return "unknown status";
+    }
+}
+
+W8A8_API const char *w8a8_last_error(void) { return g_last_error.c_str(); }

@@ -1,0 +1,50 @@
+// Internal declarations shared by the HIP translation units of libw8a8.
+// Not part of the public ABI (include/w8a8.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+// Sizes of the prepacked weight fragments (see int8_prepack_weight).
+constexpr int kFragN = 16;      // output channels per fragment
+constexpr int kFragK = 64;      // reduction elements per fragment
+constexpr int kFragBytes = 1024;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// ---- per-row quantization (quant.hip) ----
+// in_f32 = false: x is bf16 bits [rows, ldx]; true: x is fp32 [rows, ldx].
+hipError_t launch_quant_rows(const void *x, bool in_f32, int64_t rows, int64_t K, int64_t ldx,
+                             int8_t *q, int64_t ldq, float *scale, hipStream_t stream);
+
+// ---- weight repack (prepack.hip) ----
+hipError_t launch_prepack(const int8_t *wq, int64_t N, int64_t K, int64_t ldw, void *packed,
+                          hipStream_t stream);
+hipError_t launch_unpack(const void *packed, int64_t N, int64_t K, int8_t *wq, int64_t ldw,
+                         hipStream_t stream);
+
+// ---- scaled matmul (scaled_mm.hip) ----
+struct MmArgs {
+    const int8_t *xq;
+    const float *xs;
+    const int8_t *wp;
+    const float *ws;
+    const uint16_t *bias;
+    void *out;
+    int64_t ldq;
+    int64_t ldo;
+    int M, N, K;
+    int kblocks;     // round_up(K, 64) / 64: fragments along K in the packed weight
+    int nblocks;     // round_up(N, 16) / 16: fragments along N in the packed weight
+    int vec_store;   // 1 when out rows allow full-width vector stores
+};
+
+int mm_tile_count();
+const char *mm_tile_name(int tile);
+int mm_tile_auto(int64_t M, int64_t N, int64_t K);
+hipError_t launch_scaled_mm(const MmArgs &a, bool out_i32, int tile, hipStream_t stream);
+
+}  // namespace w8a8

@@ -1,0 +1,65 @@
+"""W8A8Linear: a linear layer whose forward pass runs the W8A8 int8-dynamic path.
+
+Shape handling follows the page "Diffusion Quantization Reference": its GGUF
+rules flatten N-D activations around the matmul and restore the shape, and
+its "Common Failures" table lists an output rank collapsing from 3-D to 2-D
+as a bug. Inputs [..., K] are viewed as [M, K] (no copy when the last
+dimension is contiguous) and outputs come back as [..., N].
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import ops
+
+__all__ = ["W8A8Linear"]
+
+
+class W8A8Linear(torch.nn.Module):
+    """y = bf16( int8(x) @ int8(W)^T * x_scale * w_scale (+ bias) ).
+
+    Build with ``from_float`` (per-channel weight quantization on the GPU,
+    then the load-time repack) or ``from_quantized`` (int8 weights and fp32
+    scales already made offline).
+    """
+
+    def __init__(self, w_packed: torch.Tensor, w_scale: torch.Tensor, out_features: int,
+                 in_features: int, bias: Optional[torch.Tensor] = None):
+        super().__init__()
+        self.in_features = in_features
+        self.out_features = out_features
+        self.register_buffer("w_packed", w_packed)
+        self.register_buffer("w_scale", w_scale)
+        self.register_buffer("bias", bias)
+
+    @classmethod
+    def from_quantized(cls, wq: torch.Tensor, w_scale: torch.Tensor,
+                       bias: Optional[torch.Tensor] = None) -> "W8A8Linear":
+        N, K = wq.shape
+        if not torch.isfinite(w_scale).all():
+            raise ValueError("weight scales must be finite")
+        packed = ops.prepack_weight(wq.contiguous())
+        b = None if bias is None else bias.to(torch.bfloat16).contiguous()
+        return cls(packed, w_scale.to(torch.float32).contiguous(), N, K, b)
+
+    @classmethod
+    def from_float(cls, weight: torch.Tensor, bias: Optional[torch.Tensor] = None) -> "W8A8Linear":
+        wq, ws = ops.quant_per_channel(weight.to(torch.float32).contiguous())
+        return cls.from_quantized(wq, ws, bias)
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if x.shape[-1] != self.in_features:
+            raise ValueError(f"expected last dimension {self.in_features}, got {x.shape[-1]}")
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, self.in_features)
+        if x2.stride(-1) != 1:
+            x2 = x2.contiguous()
+        xq, xs = ops.quant_per_token(x2)
+        out = ops.scaled_mm(xq, xs, self.w_packed, self.w_scale, self.out_features, self.bias)
+        return out.reshape(*lead, self.out_features)
+
+    def extra_repr(self) -> str:
+        return (f"in_features={self.in_features}, out_features={self.out_features}, "
+                f"bias={self.bias is not None}")

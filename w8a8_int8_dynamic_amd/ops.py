@@ -1,0 +1,154 @@
+"""Torch-tensor wrappers over the libw8a8 C ABI (argument marshalling only).
+
+Every step of the layer runs in the HIP kernels; these functions only check
+dtypes and devices, allocate outputs with torch, and pass raw device
+pointers, leading dimensions and torch's current HIP stream to the library.
+Tensors must be on a CUDA (HIP) device; the last dimension must be
+contiguous (stride 1); the row stride becomes the leading dimension.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import W8A8_OUT_BF16, W8A8_OUT_I32, call
+
+__all__ = ["quant_per_token", "quant_per_channel", "prepack_weight", "unpack_weight",
+           "prepack_weight_bytes", "scaled_mm", "tile_count", "tile_name", "tile_auto",
+           "device_supported"]
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _matrix(t: torch.Tensor, name: str, dtype: torch.dtype) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if t.stride(1) != 1 and t.shape[1] > 1:
+        raise ValueError(f"{name} must have a contiguous last dimension")
+    return t
+
+
+def _ld(t: torch.Tensor) -> int:
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+
+
+def _vector(t: Optional[torch.Tensor], n: int, name: str, dtype: torch.dtype):
+    if t is None:
+        return None
+    if not t.is_cuda or t.dtype != dtype or t.shape != (n,) or (n > 1 and t.stride(0) != 1):
+        raise ValueError(f"{name} must be a contiguous {dtype} device vector of length {n}")
+    return t
+
+
+def quant_per_token(x: torch.Tensor, xq: Optional[torch.Tensor] = None,
+                    xs: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-token dynamic quantization of bf16 x [M, K] -> (int8 [M, K], fp32 [M])."""
+    _matrix(x, "x", torch.bfloat16)
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if xs is None:
+        xs = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _matrix(xq, "xq", torch.int8)
+    _vector(xs, M, "xs", torch.float32)
+    with torch.cuda.device(x.device):
+        call("int8_quant_per_token", x.data_ptr(), M, K, _ld(x), xq.data_ptr(), _ld(xq),
+             xs.data_ptr(), _stream(x))
+    return xq, xs
+
+
+def quant_per_channel(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-output-channel quantization of fp32 w [N, K] -> (int8 [N, K], fp32 [N])."""
+    _matrix(w, "w", torch.float32)
+    N, K = w.shape
+    wq = torch.empty((N, K), dtype=torch.int8, device=w.device)
+    ws = torch.empty((N,), dtype=torch.float32, device=w.device)
+    with torch.cuda.device(w.device):
+        call("int8_quant_per_channel", w.data_ptr(), N, K, _ld(w), wq.data_ptr(), K,
+             ws.data_ptr(), _stream(w))
+    return wq, ws
+
+
+def prepack_weight_bytes(N: int, K: int) -> int:
+    n = _lib.lib().int8_prepack_weight_bytes(N, K)
+    if n == 0:
+        raise ValueError(f"no prepacked size for N={N}, K={K}")
+    return n
+
+
+def prepack_weight(wq: torch.Tensor) -> torch.Tensor:
+    """Repack int8 wq [N, K] into the fragment layout int8_scaled_mm reads (uint8 bytes)."""
+    _matrix(wq, "wq", torch.int8)
+    N, K = wq.shape
+    packed = torch.empty((prepack_weight_bytes(N, K),), dtype=torch.uint8, device=wq.device)
+    with torch.cuda.device(wq.device):
+        call("int8_prepack_weight", wq.data_ptr(), N, K, _ld(wq), packed.data_ptr(), _stream(wq))
+    return packed
+
+
+def unpack_weight(packed: torch.Tensor, N: int, K: int) -> torch.Tensor:
+    """Inverse of prepack_weight: int8 [N, K]."""
+    if not packed.is_cuda or packed.dtype != torch.uint8 or packed.numel() < prepack_weight_bytes(N, K):
+        raise ValueError("packed must be a uint8 device buffer from prepack_weight")
+    wq = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    with torch.cuda.device(packed.device):
+        call("int8_unpack_weight", packed.data_ptr(), N, K, wq.data_ptr(), K, _stream(packed))
+    return wq
+
+
+def scaled_mm(xq: torch.Tensor, xs: Optional[torch.Tensor], w_packed: torch.Tensor,
+              ws: Optional[torch.Tensor], N: int, bias: Optional[torch.Tensor] = None,
+              out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+              tile: int = -1) -> torch.Tensor:
+    """out[m, n] = bf16(acc * xs[m] * ws[n] (+ bias[n])), or int32 acc when out_dtype=int32."""
+    _matrix(xq, "xq", torch.int8)
+    M, K = xq.shape
+    if out_dtype == torch.bfloat16:
+        mode = W8A8_OUT_BF16
+        _vector(xs, M, "xs", torch.float32)
+        _vector(ws, N, "ws", torch.float32)
+        _vector(bias, N, "bias", torch.bfloat16)
+    elif out_dtype == torch.int32:
+        mode = W8A8_OUT_I32
+    else:
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.int32")
+    if not w_packed.is_cuda or w_packed.dtype != torch.uint8 or \
+            w_packed.numel() < prepack_weight_bytes(N, K):
+        raise ValueError("w_packed must be a uint8 device buffer from prepack_weight(N, K)")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    _matrix(out, "out", out_dtype)
+    if out.shape != (M, N):
+        raise ValueError(f"out must have shape {(M, N)}")
+
+    def ptr(t):
+        return None if t is None or mode == W8A8_OUT_I32 else t.data_ptr()
+
+    with torch.cuda.device(xq.device):
+        call("int8_scaled_mm_tile", xq.data_ptr(), _ld(xq), ptr(xs), w_packed.data_ptr(), ptr(ws),
+             ptr(bias), M, N, K, mode, out.data_ptr(), _ld(out), _stream(xq), tile)
+    return out
+
+
+def tile_count() -> int:
+    return _lib.lib().w8a8_mm_tile_count()
+
+
+def tile_name(tile: int) -> str:
+    return _lib.lib().w8a8_mm_tile_name(tile).decode()
+
+
+def tile_auto(M: int, N: int, K: int) -> int:
+    return _lib.lib().w8a8_mm_tile_auto(M, N, K)
+
+
+def device_supported(device: int = 0) -> bool:
+    return bool(_lib.lib().w8a8_device_supported(device))
