@@ -29,7 +29,8 @@ def ops():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from w8a8_int8_dynamic_amd import ops as _ops
-    assert _ops.device_supported(torch.cuda.current_device()), "not a gfx950 device"
+    from w8a8_int8_dynamic_amd import _lib
+    assert _ops.device_supported(torch.cuda.current_device()), _lib.last_error()
     return _ops
 
 

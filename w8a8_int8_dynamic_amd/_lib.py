@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(
                 f"{LIBRARY} is missing: build it with `python -m w8a8_int8_dynamic_amd.build` "
                 "(there is no fallback implementation)")
+        # torch ships its own HIP runtime. Load it first so that libw8a8 binds
+        # to that same runtime (one HIP context per process) instead of
+        # pulling in a second copy from the ROCm install.
+        import torch  # noqa: F401
         handle = ctypes.CDLL(LIBRARY)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(handle, name)

@@ -46,14 +46,21 @@ std::atomic<int> g_dev_ok[kMaxDevices];
 
 int query_supported(int device)
 {
-    if (device < 0 || device >= kMaxDevices)
+    if (device < 0 || device >= kMaxDevices) {
+        fail(W8A8_ERR_DEVICE, "device %d out of range", device);
         return 0;
+    }
     int c = g_dev_ok[device].load(std::memory_order_relaxed);
     if (c == 0) {
         hipDeviceProp_t prop;
-        if (hipGetDeviceProperties(&prop, device) != hipSuccess)
-            return 0;   // not cached: the device may become usable later
+        hipError_t e = hipGetDeviceProperties(&prop, device);
+        if (e != hipSuccess) {   // not cached: the device may become usable later
+            fail(W8A8_ERR_DEVICE, "hipGetDeviceProperties(%d): %s", device, hipGetErrorString(e));
+            return 0;
+        }
         c = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        if (c == 2)
+            fail(W8A8_ERR_DEVICE, "device %d is %s, not gfx950", device, prop.gcnArchName);
         g_dev_ok[device].store(c, std::memory_order_relaxed);
     }
     return c == 1;
@@ -66,7 +73,7 @@ w8a8_status_t check_device()
     if (e != hipSuccess)
         return fail(W8A8_ERR_DEVICE, "no current HIP device: %s", hipGetErrorString(e));
     if (!query_supported(dev))
-        return fail(W8A8_ERR_DEVICE, "device %d is not a gfx950 GPU", dev);
+        return W8A8_ERR_DEVICE;   // query_supported recorded the reason
     return W8A8_OK;
 }
 

@@ -48,13 +48,35 @@ def _vector(t: Optional[torch.Tensor], n: int, name: str, dtype: torch.dtype):
     return t
 
 
+def _round_up(a: int, b: int) -> int:
+    return -(-a // b) * b
+
+
+def _rows_aligned(t: torch.Tensor, elems: int) -> torch.Tensor:
+    """t itself when its rows start on 16-byte boundaries (row stride a multiple of
+    ``elems``), else a copy into a row-padded buffer, viewed back to t's shape."""
+    if t.data_ptr() % 16 == 0 and _ld(t) % elems == 0:
+        return t
+    M, K = t.shape
+    buf = torch.empty((M, _round_up(K, elems)), dtype=t.dtype, device=t.device)
+    buf[:, :K].copy_(t)
+    return buf[:, :K]
+
+
+def _codes(M: int, K: int, device) -> torch.Tensor:
+    """int8 [M, K] view of a buffer whose rows are padded to 16 bytes, the row
+    stride int8_scaled_mm requires."""
+    return torch.empty((M, _round_up(K, 16)), dtype=torch.int8, device=device)[:, :K]
+
+
 def quant_per_token(x: torch.Tensor, xq: Optional[torch.Tensor] = None,
                     xs: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Per-token dynamic quantization of bf16 x [M, K] -> (int8 [M, K], fp32 [M])."""
     _matrix(x, "x", torch.bfloat16)
     M, K = x.shape
+    x = _rows_aligned(x, 8)
     if xq is None:
-        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        xq = _codes(M, K, x.device)
     if xs is None:
         xs = torch.empty((M,), dtype=torch.float32, device=x.device)
     _matrix(xq, "xq", torch.int8)
@@ -69,10 +91,11 @@ def quant_per_channel(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     """Per-output-channel quantization of fp32 w [N, K] -> (int8 [N, K], fp32 [N])."""
     _matrix(w, "w", torch.float32)
     N, K = w.shape
-    wq = torch.empty((N, K), dtype=torch.int8, device=w.device)
+    w = _rows_aligned(w, 4)
+    wq = _codes(N, K, w.device)
     ws = torch.empty((N,), dtype=torch.float32, device=w.device)
     with torch.cuda.device(w.device):
-        call("int8_quant_per_channel", w.data_ptr(), N, K, _ld(w), wq.data_ptr(), K,
+        call("int8_quant_per_channel", w.data_ptr(), N, K, _ld(w), wq.data_ptr(), _ld(wq),
              ws.data_ptr(), _stream(w))
     return wq, ws
 
