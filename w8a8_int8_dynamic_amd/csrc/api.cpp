@@ -9,7 +9,7 @@
 #include <limits>
 #include <string>
 
-#include "../../include/w8a8.h"
+#include "w8a8.h"   // include/ is on the include path
 #include "internal.hpp"
 
 #define W8A8_API extern "C" __attribute__((visibility("default")))
