@@ -55,6 +55,10 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kXcds = 8;
 
@@ -67,17 +71,9 @@ __device__ __forceinline__ int xcd_remap(int pid, int tiles)
     return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
-__device__ __forceinline__ unsigned bf16_bits(float f)
-{
-    return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)f);   // RNE
-}
-
 // s_waitcnt lgkmcnt(0) only (vmcnt and expcnt untouched; gfx9 encoding):
 // this wave's LDS reads and writes have completed.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F & ~0x0F00); }
-
-// s_waitcnt for everything.
-__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
 // s_waitcnt vmcnt(VM) lgkmcnt(0).
 template <int VM>
@@ -88,11 +84,6 @@ __device__ __forceinline__ void wait_vm_lgkm0()
 }
 
 __device__ __forceinline__ int tok_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-
-__device__ __forceinline__ v4i as_v4i(const uint4 &v)
-{
-    return v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-}
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
@@ -109,34 +100,50 @@ __device__ __forceinline__ void static_for(F &&f)
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int BM_, int BN_, int WN_, int WK_, int NS_>
+constexpr int cgcd(int a, int b) { return b == 0 ? a : cgcd(b, a % b); }
+constexpr int clcm(int a, int b) { return a / cgcd(a, b) * b; }
+
+// BM x BN output tile; WN column groups x WK k-groups of wavefronts; token
+// rows fetched LT stages ahead of their LDS write, weights LW stages ahead
+// of their use.
+template <int BM_, int BN_, int WN_, int WK_, int LT_, int LW_>
 struct Tile {
-    static constexpr int BM = BM_, BN = BN_, WN = WN_, WK = WK_, NS = NS_;
+    static constexpr int BM = BM_, BN = BN_, WN = WN_, WK = WK_, LT = LT_, LW = LW_;
     static constexpr int NW = WN * WK;                 // wavefronts per workgroup
     static constexpr int THREADS = NW * 64;
     static constexpr int MB = BM / 16;                 // 16-row token images per k-block
     static constexpr int FM = BM / 32;                 // 32x32 MFMA tiles per wave, rows
     static constexpr int FN = BN / WN / 32;            // ... and columns
     static constexpr int AIMG = WK * MB;               // token images per stage
-    static constexpr int LA = AIMG / NW;               // token DMA loads per wave per stage
+    static constexpr int LA = AIMG / NW;               // token loads per wave per stage
     static constexpr int LB = 2 * FN;                  // weight loads per wave per stage
     static constexpr int LPW = LA + LB;                // global loads per wave per stage
-    static constexpr int STAGE = AIMG * 64;            // uint4 slots per ring stage
-    static constexpr int RING = NS * STAGE * 16;       // bytes
+    static constexpr int NA = LT;                      // token staging register sets
+    static constexpr int NB = LW + 1;                  // weight register sets
+    static constexpr int GROUP = clcm(clcm(NA, NB), 2);     // steps per unrolled loop body
+    static constexpr int AHEAD = cmax(LT + 2, LW);     // furthest stage a step fetches
+    // Steady-state wait at the top of a step: the token rows to be written
+    // to LDS (fetched LT steps earlier, first in their step) and the weights
+    // of this step (fetched LW steps earlier, last in their step) have landed.
+    static constexpr int VM = cmax(0, LB + (LT - 1) * LPW < (LW - 1) * LPW ? LB + (LT - 1) * LPW
+                                                                           : (LW - 1) * LPW);
+    static constexpr int STAGE = AIMG * 64;            // 16-byte slots per LDS stage
+    static constexpr int RING = 2 * STAGE * 16;        // two LDS stages, bytes
     static constexpr int PART = (WK - 1) * BM * BN * 4;     // k-group partial sums
     static constexpr int PITCH = BN * 2 + 8;           // staged bf16 row, bytes
     static constexpr int OUTB = BM * PITCH;
-    static constexpr int LDS = cmax(RING, cmax(PART, OUTB));
+    static constexpr int MAIN = cmax(RING, cmax(PART, OUTB));
+    static constexpr int SIDE = 2 * BN + BM;           // fp32 ws, bias, xs of the tile
+    static constexpr int SIDE_PER_THREAD = (SIDE + THREADS - 1) / THREADS;
+    static constexpr int LDS = MAIN + SIDE * 4;
     static_assert(NW == 4, "four wavefronts per workgroup");
     static_assert(BM % 32 == 0 && BN % (32 * WN) == 0, "tile/wave mismatch");
     static_assert(AIMG % NW == 0, "token loads must split evenly over waves");
-    static_assert(NS == 3 || NS == 4, "pipeline depth: 3 or 4 stages");
-    static_assert(LA * 0 + (2 * (BN / WN / 32) + (WK * (BM / 16)) / (WN * WK)) * (NS - 2) < 64,
-                  "vmcnt range");
-    static constexpr int NA = NS - 2;                  // token staging register sets
-    static constexpr int GROUP = NS == 4 ? 4 : 3;      // lcm(NS, NA): steps per unrolled group
+    static_assert(LT >= 2 && LW >= LT, "token lead >= 2, weight lead >= token lead");
+    static_assert(VM < 64 && (LW + LT) * LPW < 64, "vmcnt range");
     static_assert(LDS <= 160 * 1024, "LDS budget");
     static_assert(FM * FN * 16 <= 256, "accumulators must fit the AGPR file");
+    static_assert(WK <= 2 && FM % WK == 0, "k-groups split the row tiles evenly");
 };
 
 template <class T, bool OUT_I32>
@@ -189,24 +196,49 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs a)
         xslot[h] = ((lane >> 4) & 1) * 64 + 4 * r16 + (c ^ tok_swz(r16));
     }
 
+    // Scales (and bias) of the tile, fetched now into a couple of registers
+    // per thread and parked in LDS for the epilogue, so that their latency
+    // hides behind the K loop: entries [0, BN) ws, [BN, 2BN) bias as fp32
+    // (zero without bias), [2BN, 2BN+BM) xs; rows/channels past M/N repeat
+    // the last valid one.
+    float side_v[T::SIDE_PER_THREAD];
+    if (!OUT_I32) {
+#pragma unroll
+        for (int u = 0; u < T::SIDE_PER_THREAD; ++u) {
+            const int p = u * T::THREADS + (int)threadIdx.x;
+            float v = 0.0f;
+            if (p < T::BN)
+                v = a.ws[min(n0 + p, a.N - 1)];
+            else if (p < 2 * T::BN) {
+                if (a.bias)
+                    v = __uint_as_float((unsigned)a.bias[min(n0 + p - T::BN, a.N - 1)] << 16);
+            } else if (p < T::SIDE)
+                v = a.xs[min(m0 + p - 2 * T::BN, a.M - 1)];
+            side_v[u] = v;
+        }
+    }
+
     v16i acc[T::FN][T::FM];
 #pragma unroll
     for (int j = 0; j < T::FN; ++j)
 #pragma unroll
         for (int i = 0; i < T::FM; ++i)
             acc[j][i] = v16i{};
-    v4i bq[T::NS][T::FN][2];                           // weight operand ring
+    v4i bq[T::NB][T::FN][2];                           // weight operand ring
     v4i ast[T::NA][T::LA];                             // token staging ring
-    v4i xf[T::FM][2];                                  // token operands of one stage
+    v4i xf[2][T::FM][2];                               // token operands, this and next stage
 
-    // Global loads of stage t: token rows into staging set t % NA, weights
-    // into ring set t % NS.
-    auto load = [&](int t, v4i (&aset)[T::LA], v4i (&bset)[T::FN][2]) __attribute__((always_inline)) {
+    // Global loads: token rows of stage t into staging set t % NA; weights of
+    // stage t into ring set t % NB. Addresses are clamped into the operands,
+    // so a load of a stage past the end is harmless.
+    auto load_a = [&](int t, v4i (&aset)[T::LA]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < T::LA; ++i) {
             const int kc = min((t * T::WK + aks[i]) * 64 + dchunk, klast);
             aset[i] = *reinterpret_cast<const v4i *>(arow[i] + kc);
         }
+    };
+    auto load_b = [&](int t, v4i (&bset)[T::FN][2]) __attribute__((always_inline)) {
         const int kb = min(t * T::WK + wk, kblast);
 #pragma unroll
         for (int j = 0; j < T::FN; ++j)
@@ -214,129 +246,170 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs a)
             for (int h = 0; h < 2; ++h)
                 bset[j][h] = bsrc[j][(int64_t)kb * 64 + h * 32];
     };
-    // Token rows of stage t from staging registers into LDS ring buffer t % NS.
+    // Token rows of stage t from staging registers into LDS stage t % 2.
     auto store = [&](int t, const v4i (&aset)[T::LA]) __attribute__((always_inline)) {
-        v4i *st = reinterpret_cast<v4i *>(lds) + (t % T::NS) * T::STAGE;
+        v4i *st = reinterpret_cast<v4i *>(lds) + (t & 1) * T::STAGE;
 #pragma unroll
         for (int i = 0; i < T::LA; ++i)
             st[(i * T::NW + wave) * 64 + lane] = aset[i];
     };
-
-    // One stage s: barrier (stage s is in LDS and stage s-2's buffer is
-    // free), move stage s+1 into LDS, fetch stage s+NS-1, read this wave's
-    // token operands of stage s, run its MFMAs. In the steady state (FULL)
-    // every step is unconditional.
-    auto step = [&](auto full, int s, v4i (&anext)[T::LA], v4i (&bcur)[T::FN][2],
-                    v4i (&bnext)[T::FN][2]) __attribute__((always_inline)) {
-        constexpr bool FULL = decltype(full)::value;
-        // Stage s's weights were fetched NS-1 steps ago; LPW*(NS-2) loads of
-        // later stages may still be in flight. (Stated explicitly: at the
-        // loop back-edge the compiler's own count otherwise degrades to a
-        // full drain.)
-        if (FULL)
-            wait_vm_lgkm0<T::LPW * (T::NS - 2)>();
-        else
-            wait_lgkm0();
-        __builtin_amdgcn_s_barrier();
-        if (FULL || s + 1 < S)
-            store(s + 1, anext);
-        if (FULL || s + T::NS - 1 < S)
-            load(s + T::NS - 1, anext, bnext);
-        const v4i *st = reinterpret_cast<const v4i *>(lds) + (s % T::NS) * T::STAGE + wk * T::MB * 64;
+    // This wave's token operands of stage t (its k-group's k-block) from LDS.
+    auto read = [&](int t, v4i (&x)[T::FM][2]) __attribute__((always_inline)) {
+        const v4i *st = reinterpret_cast<const v4i *>(lds) + (t & 1) * T::STAGE + wk * T::MB * 64;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < T::FM; ++i)
-                xf[i][h] = st[(2 * i) * 64 + xslot[h]];
-        if (FULL || s * T::WK + wk < a.kblocks) {
+                x[i][h] = st[(2 * i) * 64 + xslot[h]];
+    };
+    auto mma = [&](const v4i (&x)[T::FM][2], const v4i (&b)[T::FN][2]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int j = 0; j < T::FN; ++j)
+            for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-                    for (int i = 0; i < T::FM; ++i)
-                        acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bcur[j][h], xf[i][h],
-                                                                          acc[j][i], 0, 0, 0);
-        }
+                for (int i = 0; i < T::FM; ++i)
+                    acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j][h], x[i][h], acc[j][i], 0, 0, 0);
+    };
+
+    // Step s. On entry stage s+1 is being written to LDS by every wave, this
+    // wave's operands of stage s are in xf[s & 1], token rows of stage s+2
+    // sit in staging set (s+2) % NA and the weights of stage s in ring set
+    // s % NB. The step: barrier (stage s+1 visible; every read of stage s
+    // done), read stage s+1's operands, write stage s+2 to the LDS buffer
+    // stage s used, fetch tokens of stage s+2+LT and weights of stage s+LW,
+    // then run stage s's MFMAs.
+    auto step = [&](auto full, int s, auto u_c) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full)::value;
+        constexpr int u = decltype(u_c)::value;        // s modulo GROUP
+        if (FULL)
+            wait_vm_lgkm0<T::VM>();
+        else
+            wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+        if (FULL || s + 1 < S)
+            read(s + 1, xf[(u + 1) & 1]);
+        if (FULL || s + 2 < S)
+            store(s + 2, ast[(u + 2) % T::NA]);
+        if (FULL || s + 2 + T::LT < S)
+            load_a(s + 2 + T::LT, ast[(u + 2) % T::NA]);
+        if (FULL || s + T::LW < S)
+            load_b(s + T::LW, bq[(u + T::LW) % T::NB]);
+        if (FULL || s * T::WK + wk < a.kblocks)
+            mma(xf[u & 1], bq[u % T::NB]);
         // Keep each step's loads in program order relative to the next
-        // step, so the load counter state at the loop back-edge matches the
-        // prologue's and the compiler's waits stay exact.
+        // step, so the load counter pattern repeats exactly.
         __builtin_amdgcn_sched_barrier(0);
     };
     using Full = std::integral_constant<bool, true>;
     using Part = std::integral_constant<bool, false>;
 
-    // Prologue: stage 0 into LDS; stages 1 .. NS-2 in flight.
-    load(0, ast[0], bq[0]);
-    store(0, ast[0]);
-    static_for<T::NS - 2>([&](auto U) __attribute__((always_inline)) {
-        constexpr int t = decltype(U)::value + 1;
-        if (t < S)
-            load(t, ast[t % T::NA], bq[t]);
+    // Prologue: stages 0 and 1 into LDS, stage 0's operands into xf[0], and
+    // the loads that steps -LT .. -1 would have issued. Every load is issued
+    // even when its stage does not exist, so the load counter state at the
+    // loop entry matches the one at the back-edge and the waits the
+    // compiler derives inside the loop stay as loose as the steady state.
+    load_a(0, ast[0]);
+    load_a(1, ast[1 % T::NA]);
+    static_for<T::LW - T::LT>([&](auto U) __attribute__((always_inline)) {
+        constexpr int t = decltype(U)::value;
+        load_b(t, bq[t % T::NB]);
     });
-    // Steady state: groups of GROUP steps whose loads (stage s+NS-1 < S)
-    // and k-blocks (stage s < S-1) all exist. Step s moves stage s+1 out of
-    // staging set (s+1) % NA and refills that same set with stage s+NS-1.
+    store(0, ast[0]);
+    store(1, ast[1 % T::NA]);
+    static_for<T::LT>([&](auto U) __attribute__((always_inline)) {
+        constexpr int v = decltype(U)::value - T::LT;  // virtual step -LT .. -1
+        load_a(v + 2 + T::LT, ast[(v + 2 + T::LT) % T::NA]);
+        load_b(v + T::LW, bq[(v + T::LW) % T::NB]);
+    });
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    read(0, xf[0]);
+
+    // Steady state: GROUP unconditional steps while every stage they fetch
+    // exists.
     int s0 = 0;
-    for (; s0 + T::GROUP + T::NS - 1 <= S; s0 += T::GROUP) {
+    for (; s0 + T::GROUP + T::AHEAD <= S; s0 += T::GROUP) {
         static_for<T::GROUP>([&](auto U) __attribute__((always_inline)) {
-            constexpr int u = decltype(U)::value;
-            step(Full{}, s0 + u, ast[(u + 1) % T::NA], bq[u % T::NS], bq[(u + T::NS - 1) % T::NS]);
+            step(Full{}, s0 + decltype(U)::value, U);
         });
     }
-    // Tail: fewer than GROUP + NS - 1 stages, each guarded.
-    static_for<T::GROUP + T::NS - 1>([&](auto U) __attribute__((always_inline)) {
-        constexpr int u = decltype(U)::value;
-        if (s0 + u < S)
-            step(Part{}, s0 + u, ast[(u + 1) % T::NA], bq[u % T::NS], bq[(u + T::NS - 1) % T::NS]);
+    // Tail: fewer than GROUP + AHEAD stages, each step guarded.
+    static_for<T::GROUP + T::AHEAD>([&](auto U) __attribute__((always_inline)) {
+        if (s0 + decltype(U)::value < S)
+            step(Part{}, s0 + decltype(U)::value, U);
     });
 
     // ---- epilogue ----
     // Accumulator layout: acc[j][i] register 4q+r of lane l holds channel
     // n = 32*(wn*FN+j) + 8q + 4*(l/32) + r and token m = 32*i + l%32 of the tile.
-    wait_all();
-    __builtin_amdgcn_s_barrier();                      // ring fully consumed
-    if (T::WK > 1) {
-        uint4 *part = lds;
-        constexpr int PW = T::FN * T::FM * 4 * 64;     // uint4 slots per wave's partials
-        if (wk > 0) {
+    // k-group wk finishes row tiles i in [wk*FMH, (wk+1)*FMH): it receives the
+    // other k-group's partial sums of those through LDS and hands over its own
+    // partial sums of the rest, so all four waves share the scaling and stores.
+    constexpr int FMH = T::FM / T::WK;
+    // The accumulator registers of a wave's rows must be named at compile
+    // time, so the epilogue is instantiated once per k-group.
+    auto epilogue = [&](auto wk_c) __attribute__((always_inline)) {
+        constexpr int WKI = decltype(wk_c)::value;
+        constexpr int i0 = WKI * FMH;
+        float *side = reinterpret_cast<float *>(reinterpret_cast<char *>(lds) + T::MAIN);
+        const bool has_bias = !OUT_I32 && a.bias != nullptr;
+        if (!OUT_I32) {
 #pragma unroll
-            for (int j = 0; j < T::FN; ++j)
-#pragma unroll
-                for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const v16i &c = acc[j][i];
-                        part[((wk - 1) * T::WN + wn) * PW + ((j * T::FM + i) * 4 + q) * 64 + lane] =
-                            make_uint4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
-                    }
+            for (int u = 0; u < T::SIDE_PER_THREAD; ++u) {
+                const int p = u * T::THREADS + (int)threadIdx.x;
+                if (p < T::SIDE)
+                    side[p] = side_v[u];
+            }
         }
-        wait_all();
-        __builtin_amdgcn_s_barrier();
-        if (wk == 0) {
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();                  // every wave is done with the ring
+
+        // The other k-group's partial sums of this wave's rows, one 16-byte
+        // slot per (j, i % FMH, q, lane) of each (column group, owner).
+        v4i pv[FMH][T::FN][4];
+        if (T::WK > 1) {
+            v4i *part = reinterpret_cast<v4i *>(lds);
+            constexpr int PW = T::FN * FMH * 4 * 64;
 #pragma unroll
-            for (int g = 1; g < T::WK; ++g)
+            for (int i = 0; i < T::FM; ++i) {
+                if (i / FMH == WKI)
+                    continue;
 #pragma unroll
                 for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-                    for (int i = 0; i < T::FM; ++i)
+                    for (int q = 0; q < 4; ++q) {
+                        const v16i &c = acc[j][i];
+                        part[(wn * T::WK + i / FMH) * PW + ((j * FMH + i % FMH) * 4 + q) * 64 + lane] =
+                            v4i{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
+                    }
+            }
+            wait_lgkm0();
+            __builtin_amdgcn_s_barrier();
+            // All reads first, one wait: they are independent.
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const uint4 v =
-                                part[((g - 1) * T::WN + wn) * PW + ((j * T::FM + i) * 4 + q) * 64 + lane];
-                            acc[j][i][4 * q] += (int)v.x;
-                            acc[j][i][4 * q + 1] += (int)v.y;
-                            acc[j][i][4 * q + 2] += (int)v.z;
-                            acc[j][i][4 * q + 3] += (int)v.w;
-                        }
+            for (int i = 0; i < FMH; ++i)
+#pragma unroll
+                for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        pv[i][j][q] = part[(wn * T::WK + WKI) * PW + ((j * FMH + i) * 4 + q) * 64 + lane];
+        } else {
+#pragma unroll
+            for (int i = 0; i < FMH; ++i)
+#pragma unroll
+                for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        pv[i][j][q] = v4i{};
         }
-        wait_all();
-        __builtin_amdgcn_s_barrier();                  // partials consumed: LDS reusable
-    }
+        // Final int32 sums of this wave's outputs.
+        auto sum = [&](int i, int j, int q, int r) __attribute__((always_inline)) {
+            return acc[j][i0 + i][4 * q + r] + pv[i][j][q][r];
+        };
 
-    if (OUT_I32) {
-        // Debug mode: raw accumulators straight from registers.
-        if (wk == 0) {
+        if (OUT_I32) {
+            // Debug mode: raw accumulators straight from registers.
 #pragma unroll
             for (int j = 0; j < T::FN; ++j)
 #pragma unroll
@@ -346,79 +419,115 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs a)
                         continue;
                     const bool full = a.vec_store && n + 3 < a.N;
 #pragma unroll
-                    for (int i = 0; i < T::FM; ++i) {
-                        const int m = m0 + i * 32 + (lane & 31);
+                    for (int i = 0; i < FMH; ++i) {
+                        const int m = m0 + (i0 + i) * 32 + (lane & 31);
                         if (m >= a.M)
                             continue;
-                        const v16i &c = acc[j][i];
                         int *o = reinterpret_cast<int *>(a.out) + (int64_t)m * a.ldo + n;
                         if (full) {
-                            *reinterpret_cast<int4 *>(o) =
-                                make_int4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
+                            *reinterpret_cast<v4i *>(o) = v4i{sum(i, j, q, 0), sum(i, j, q, 1),
+                                                              sum(i, j, q, 2), sum(i, j, q, 3)};
                         } else {
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
                                 if (n + r < a.N)
-                                    o[r] = c[4 * q + r];
+                                    o[r] = sum(i, j, q, r);
                         }
                     }
                 }
+            return;
         }
-        return;
-    }
 
-    // bf16 output: scale in registers, stage the BM x BN tile in LDS (row
-    // pitch BN*2+8 bytes keeps the 8-byte writes of 32 rows on distinct
-    // banks), then write whole rows: consecutive lanes store consecutive
-    // 8-byte pieces, so every store instruction fills complete cache lines.
-    char *tile_lds = reinterpret_cast<char *>(lds);
-    if (wk == 0) {
+        // bf16 output. Scales of this wave's columns and rows from LDS (all
+        // reads issued together), then the epilogue's fixed order per output:
+        // acc * xs, then * ws, then + bias, each step rounded to fp32, and a
+        // round-to-nearest-even pair conversion to bf16.
+        f32x4 w4[T::FN][4];
+        float xr[FMH];
 #pragma unroll
-        for (int i = 0; i < T::FM; ++i) {
-            const int ml = i * 32 + (lane & 31);
-            const float xs = a.xs[min(m0 + ml, a.M - 1)];
+        for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-            for (int j = 0; j < T::FN; ++j) {
+            for (int q = 0; q < 4; ++q)
+                w4[j][q] = *reinterpret_cast<const f32x4 *>(side + (wn * T::FN + j) * 32 + q * 8 + (lane >> 5) * 4);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int nl = (wn * T::FN + j) * 32 + q * 8 + (lane >> 5) * 4;
-                    const v16i &c = acc[j][i];
-                    unsigned h[4];
+        for (int i = 0; i < FMH; ++i)
+            xr[i] = side[2 * T::BN + (i0 + i) * 32 + (lane & 31)];
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();                  // partials consumed: LDS reusable
+
+        // Stage the BM x BN bf16 tile in LDS (row pitch BN*2+8 bytes keeps
+        // the 8-byte writes of 32 rows on distinct banks) ...
+        char *tile_lds = reinterpret_cast<char *>(lds);
+        auto scale = [&](auto with_bias) __attribute__((always_inline)) {
+            constexpr bool B = decltype(with_bias)::value;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int nn = min(n0 + nl + r, a.N - 1);
-                        float t = (float)c[4 * q + r] * xs;
-                        t = t * a.ws[nn];
-                        if (a.bias)
-                            t = t + __uint_as_float((unsigned)a.bias[nn] << 16);
-                        h[r] = bf16_bits(t);
+            for (int i = 0; i < FMH; ++i) {
+                const int ml = (i0 + i) * 32 + (lane & 31);
+#pragma unroll
+                for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int nl = (wn * T::FN + j) * 32 + q * 8 + (lane >> 5) * 4;
+                        const f32x4 b4 = B ? *reinterpret_cast<const f32x4 *>(side + T::BN + nl) : f32x4{};
+                        float t[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            t[r] = (float)sum(i, j, q, r) * xr[i];
+                            t[r] = t[r] * w4[j][q][r];
+                            if (B)
+                                t[r] = t[r] + b4[r];
+                        }
+                        const bf16x2 lo = __builtin_convertvector((f32x2){t[0], t[1]}, bf16x2);
+                        const bf16x2 hi = __builtin_convertvector((f32x2){t[2], t[3]}, bf16x2);
+                        *reinterpret_cast<v2u *>(tile_lds + ml * T::PITCH + nl * 2) =
+                            v2u{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
                     }
-                    *reinterpret_cast<uint2 *>(tile_lds + ml * T::PITCH + nl * 2) =
-                        make_uint2(h[0] | h[1] << 16, h[2] | h[3] << 16);
-                }
+            }
+        };
+        if (has_bias)
+            scale(std::true_type{});
+        else
+            scale(std::false_type{});
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+
+        // ... then write whole rows: consecutive lanes store consecutive
+        // 8-byte pieces, so every store instruction fills complete cache
+        // lines. All LDS reads are issued before the first store.
+        constexpr int QPR = T::BN / 4;                 // 8-byte pieces per row
+        constexpr int PIECES = T::BM * QPR;
+        constexpr int ITER = (PIECES + T::THREADS - 1) / T::THREADS;
+        v2u val[ITER];
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+            const int p = it * T::THREADS + (int)threadIdx.x;
+            if (PIECES % T::THREADS == 0 || p < PIECES)
+                val[it] = *reinterpret_cast<const v2u *>(tile_lds + (p / QPR) * T::PITCH + (p % QPR) * 8);
+        }
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+            const int p = it * T::THREADS + (int)threadIdx.x;
+            const int m = m0 + p / QPR, n = n0 + (p % QPR) * 4;
+            if ((PIECES % T::THREADS != 0 && p >= PIECES) || m >= a.M || n >= a.N)
+                continue;
+            uint16_t *o = reinterpret_cast<uint16_t *>(a.out) + (int64_t)m * a.ldo + n;
+            const v2u v = val[it];
+            if (a.vec_store && n + 3 < a.N) {
+                *reinterpret_cast<v2u *>(o) = v;
+            } else {
+                const unsigned hv[4] = {v[0] & 0xffffu, v[0] >> 16, v[1] & 0xffffu, v[1] >> 16};
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < a.N)
+                        o[r] = (uint16_t)hv[r];
             }
         }
-    }
-    wait_all();
-    __builtin_amdgcn_s_barrier();
-    constexpr int QPR = T::BN / 4;                     // 8-byte pieces per row
-    for (int p = threadIdx.x; p < T::BM * QPR; p += T::THREADS) {
-        const int ml = p / QPR, nl = (p % QPR) * 4;
-        const int m = m0 + ml, n = n0 + nl;
-        if (m >= a.M || n >= a.N)
-            continue;
-        const uint2 v = *reinterpret_cast<const uint2 *>(tile_lds + ml * T::PITCH + nl * 2);
-        uint16_t *o = reinterpret_cast<uint16_t *>(a.out) + (int64_t)m * a.ldo + n;
-        if (a.vec_store && n + 3 < a.N) {
-            *reinterpret_cast<uint2 *>(o) = v;
-        } else {
-            const unsigned hv[4] = {v.x & 0xffffu, v.x >> 16, v.y & 0xffffu, v.y >> 16};
-            for (int r = 0; r < 4; ++r)
-                if (n + r < a.N)
-                    o[r] = (uint16_t)hv[r];
-        }
-    }
+    };
+    static_for<T::WK>([&](auto W) __attribute__((always_inline)) {
+        if (wk == decltype(W)::value)
+            epilogue(W);
+    });
 }
+
 
 typedef void (*MmFn)(const MmArgs);
 
@@ -434,14 +543,15 @@ constexpr TileEntry entry(const char *name)
     return TileEntry{name, T::BM, T::BN, scaled_mm_kernel<T, false>, scaled_mm_kernel<T, true>};
 }
 
-// BM x BN output tile / WN column groups x WK k-groups of waves / NS stages
+// BM x BN output tile / WN column groups x WK k-groups of waves / token and
+// weight fetch leads in stages
 const TileEntry kTiles[] = {
-    entry<Tile<64, 64, 2, 2, 4>>("64x64/n2k2/s4"),
-    entry<Tile<64, 128, 2, 2, 4>>("64x128/n2k2/s4"),
-    entry<Tile<128, 64, 2, 2, 4>>("128x64/n2k2/s4"),
-    entry<Tile<128, 128, 2, 2, 4>>("128x128/n2k2/s4"),
-    entry<Tile<128, 192, 2, 2, 3>>("128x192/n2k2/s3"),
-    entry<Tile<128, 192, 2, 2, 4>>("128x192/n2k2/s4"),
+    entry<Tile<64, 64, 2, 2, 2, 3>>("64x64/n2k2/l23"),
+    entry<Tile<64, 128, 2, 2, 2, 3>>("64x128/n2k2/l23"),
+    entry<Tile<128, 64, 2, 2, 2, 3>>("128x64/n2k2/l23"),
+    entry<Tile<128, 128, 2, 2, 2, 3>>("128x128/n2k2/l23"),
+    entry<Tile<128, 192, 2, 2, 2, 2>>("128x192/n2k2/l22"),
+    entry<Tile<128, 192, 2, 2, 2, 3>>("128x192/n2k2/l23"),
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
