@@ -45,8 +45,9 @@ def parse_args(argv=None):
                    help="target wall time of the oracle's sampled GEMM")
     p.add_argument("--no-quant-large", action="store_true",
                    help="skip the quant bandwidth run on the FFN-down activations")
-    p.add_argument("--only", choices=["step", "mm", "quant"], default=None,
-                   help="launch only this part in a loop (for profiler runs)")
+    p.add_argument("--only", choices=["step", "mm", "quant", "copy"], default=None,
+                   help="launch only this part in a loop (for profiler runs); 'copy' is a "
+                        "plain 256 MiB device copy kernel, the calibration for HBM byte counters")
     return p.parse_args(argv)
 
 
@@ -97,42 +98,75 @@ def dev_bf16(torch, bits: np.ndarray):
 def cpu_baseline(w, inp, target_s: float) -> dict:
     """The oracle (as it stands) on a bounded sample of the workload.
 
-    Times the full per-token quant, then the exact int32 GEMM and the epilogue
-    on a sample of token rows sized to take about target_s seconds, and scales
-    the GEMM/epilogue time to all M rows. Returns int8 TOP/s of 2*M*N*K.
+    A step of the oracle is the full per-token quant, the exact int32 GEMM and
+    the fp32 epilogue. When one full step takes less than target_s seconds,
+    whole steps are repeated until target_s has passed and the mean is taken;
+    otherwise the GEMM and epilogue run on a sample of token rows sized to
+    about target_s seconds and are scaled to all M rows. Returns int8 TOP/s of
+    2*M*N*K per step.
     """
     import oracle
     o = oracle.load()
     wq, ws = o.quant_per_channel(inp.w_f32)        # offline weight prep, not timed
-    t0 = time.perf_counter()
-    xq, xs = o.quant_per_token(inp.x_bf16)
-    t_quant = time.perf_counter() - t0
     rng = np.random.default_rng(w.seed)
+
+    def step(rows):
+        t0 = time.perf_counter()
+        xq, xs = o.quant_per_token(inp.x_bf16)
+        t1 = time.perf_counter()
+        acc = o.gemm_i32(xq, wq, rows)
+        o.epilogue_f32(acc, xs if rows is None else xs[rows], ws, inp.bias_bf16)
+        return t1 - t0, time.perf_counter() - t1
+
+    xq, _ = o.quant_per_token(inp.x_bf16)
     probe = np.sort(rng.choice(w.M, min(w.M, 4), replace=False))
     t0 = time.perf_counter()
     o.gemm_i32(xq, wq, probe)
     per_row = (time.perf_counter() - t0) / len(probe)
-    n_rows = int(min(w.M, max(4, target_s / max(per_row, 1e-9))))
-    rows = np.sort(rng.choice(w.M, n_rows, replace=False))
-    t0 = time.perf_counter()
-    acc = o.gemm_i32(xq, wq, rows)
-    t_gemm = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    o.epilogue_f32(acc, xs[rows], ws, inp.bias_bf16)
-    t_epi = time.perf_counter() - t0
-    scale = w.M / n_rows
-    t_total = t_quant + (t_gemm + t_epi) * scale
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    if per_row * w.M < target_s / 2:
+        reps, t_sum, start = 0, 0.0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - start < target_s:
+            tq, tg = step(None)
+            t_sum += tq + tg
+            reps += 1
+        t_total = t_sum / reps
+        sample = (f"{reps} full oracle steps (per-token quant of X [{w.M},{w.K}], exact int32 "
+                  f"GEMM and fp32 epilogue on all rows), {t_sum:.1f} s measured, mean per step")
+    else:
+        n_rows = int(min(w.M, max(4, target_s / 2 / max(per_row, 1e-9))))
+        rows = np.sort(rng.choice(w.M, n_rows, replace=False))
+        reps, tq_sum, tg_sum, start = 0, 0.0, 0.0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - start < target_s:
+            tq, tg = step(rows)
+            tq_sum, tg_sum, reps = tq_sum + tq, tg_sum + tg, reps + 1
+        scale = w.M / n_rows
+        t_total = (tq_sum + tg_sum * scale) / reps
+        sample = (f"{reps} x (full per-token quant of X [{w.M},{w.K}] plus exact int32 GEMM "
+                  f"and fp32 epilogue on {n_rows} of {w.M} token rows, x{scale:.2f} to all "
+                  f"rows); {tq_sum + tg_sum:.1f} s measured, mean per step")
     return {
         "value": round(w.ops / t_total / 1e12, 6),
         "unit": "TOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"full per-token quant of X [{w.M},{w.K}] plus exact int32 GEMM and fp32 "
-                   f"epilogue on {n_rows} of {w.M} token rows (x{scale:.2f} to all rows); "
-                   f"{t_quant + t_gemm + t_epi:.1f} s measured"),
-        "seconds_full_step_estimate": round(t_total, 3),
+        "sample": sample,
+        "seconds_per_step": round(t_total, 4),
     }
+
+
+def copy_reference(torch, steps: int) -> dict:
+    """A plain device copy kernel (torch neg) over 256 MiB in and 256 MiB out:
+    the achievable-bandwidth reference for the HBM-bound quant pass."""
+    src = torch.ones((64 << 20,), dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    ms = time_loop(torch, lambda: torch.neg(src, out=dst), max(10, min(steps, 50)))
+    nbytes = 2 * src.numel() * 4
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"gbps": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes,
+            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
 
 
 def traffic_record(kernel: str, workload: str):
@@ -176,7 +210,6 @@ def main(argv=None) -> int:
     bias = None if inp.bias_bf16 is None else dev_bf16(torch, inp.bias_bf16)
     wq, ws = ops.quant_per_channel(torch.from_numpy(inp.w_f32).cuda())   # load time
     packed = ops.prepack_weight(wq)
-    del wq
     xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
     xs = torch.empty((M,), dtype=torch.float32, device="cuda")
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
@@ -194,12 +227,19 @@ def main(argv=None) -> int:
         mm()
 
     if args.only:
-        fn = {"step": step, "mm": mm, "quant": quant}[args.only]
+        copy_src = copy_dst = None
+        if args.only == "copy":
+            copy_src = torch.ones((64 << 20,), dtype=torch.float32, device="cuda")
+            copy_dst = torch.empty_like(copy_src)
+        fn = {"step": step, "mm": mm, "quant": quant,
+              "copy": lambda: torch.neg(copy_src, out=copy_dst)}[args.only]
         for _ in range(args.warmup + args.steps):
             fn()
         torch.cuda.synchronize()
         print(json.dumps({"only": args.only, "launches": args.warmup + args.steps,
-                          "workload": w.name, "tile": ops.tile_name(tile)}), flush=True)
+                          "workload": w.name, "tile": ops.tile_name(tile),
+                          "copy_bytes_each_way": None if copy_src is None else
+                          copy_src.numel() * 4}), flush=True)
         return 0
 
     for _ in range(args.warmup):
@@ -219,6 +259,20 @@ def main(argv=None) -> int:
     it = iter(range(1 << 30))
     ms_mm_cold = time_loop(torch, lambda: cold_calls[next(it) % len(cold_calls)](), args.steps)
     del cold_packs, cold_calls
+
+    # Context only: the vendor library's int8 GEMM (torch._int_mm, int32
+    # output, no scale epilogue) on the same operands.
+    vendor = None
+    try:
+        wt = wq.t()
+        torch._int_mm(xq, wt)
+        vendor_ms = time_loop(torch, lambda: torch._int_mm(xq, wt), args.steps)
+        vendor = {"op": "torch._int_mm(xq [M,K], wq[N,K].T) -> int32, no epilogue",
+                  "us": round(vendor_ms * 1e3, 3),
+                  "tops": round(2 * M * N * K / (vendor_ms * 1e-3) / 1e12, 2)}
+    except Exception as ex:                        # not every shape is supported
+        vendor = {"op": "torch._int_mm", "error": str(ex)[:160]}
+    del wq
 
     quant_bytes = 3 * M * K + 4 * M
     mm_ops = 2 * M * N * K
@@ -257,11 +311,13 @@ def main(argv=None) -> int:
             "frac": round(achieved / PEAK_INT8_TOPS, 4),
             "traffic": traffic_record("int8_scaled_mm", w.name),
         },
+        "vendor_int8_gemm": vendor,
         "source_digest": source_digest(),
     }
 
     if not args.no_quant_large:
         rec["quant_large"] = quant_bandwidth(torch, L, wl, stream, args.steps)
+        rec["hbm_copy_reference"] = copy_reference(torch, args.steps)
     del x, xq, xs, out, packed
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
@@ -296,7 +352,8 @@ def quant_bandwidth(torch, L, wl, stream, steps: int) -> dict:
     torch.cuda.empty_cache()
     return {"workload": w.description, "us": round(ms * 1e3, 3), "gbps": round(gbps, 1),
             "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4), "bytes": nbytes,
-            "buffers": "3 rotating sets (906 MB)"}
+            "buffers": "3 rotating sets (906 MB)",
+            "traffic": traffic_record("int8_quant_per_token", w.name)}
 
 
 if __name__ == "__main__":

@@ -160,7 +160,9 @@ w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const float *x_
                                   const uint16_t *bias, int64_t M, int64_t N, int64_t K, int mode,
                                   void *out, int64_t ldo, void *stream, int tile);
 
-/* Number of tile configurations, a short name of one ("128x128x128/2x2"),
+/* Number of tile configurations, a short name of one ("128x192/n2k2/l23":
+ * tile rows x columns / wave column groups and k-groups / token and weight
+ * fetch leads in stages),
  * and the tile the automatic choice picks for a shape. */
 int w8a8_mm_tile_count(void);
 const char *w8a8_mm_tile_name(int tile);
