@@ -231,6 +231,7 @@ W8A8_API w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const 
     // row start (and channel multiples of 4) aligned to that width.
     const uintptr_t vw = 4 * esz;
     a.vec_store = aligned(out, vw) && ((uint64_t)ldo * esz) % vw == 0;
+    a.vec16 = aligned(out, 16) && ((uint64_t)ldo * esz) % 16 == 0;
     return launched(w8a8::launch_scaled_mm(a, i32, t, reinterpret_cast<hipStream_t>(stream)), what);
 }
 

@@ -39,7 +39,8 @@ struct MmArgs {
     int M, N, K;
     int kblocks;     // round_up(K, 64) / 64: fragments along K in the packed weight
     int nblocks;     // round_up(N, 16) / 16: fragments along N in the packed weight
-    int vec_store;   // 1 when out rows allow full-width vector stores
+    int vec_store;   // 1 when out rows allow stores of 4 consecutive elements
+    int vec16;       // 1 when out rows start on 16-byte boundaries
 };
 
 int mm_tile_count();

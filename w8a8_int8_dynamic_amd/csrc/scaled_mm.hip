@@ -58,6 +58,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kXcds = 8;
@@ -86,6 +87,25 @@ __device__ __forceinline__ void wait_vm_lgkm0()
 __device__ __forceinline__ int tok_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// A kernel argument held in scalar registers from here on. Left alone, the
+// compiler re-reads kernel arguments from memory wherever it needs them
+// (each re-read a scalar load plus a wait) instead of keeping them.
+template <class V>
+__device__ __forceinline__ V pinned(V v)
+{
+    asm volatile("" : "+s"(v));
+    return v;
+}
+// The same for a global-memory pointer: the value passes through an
+// integer, so it is converted back through the global address space, which
+// keeps its loads and stores global (not flat) instructions.
+template <class P>
+__device__ __forceinline__ P *pinned_ptr(P *p)
+{
+    typedef __attribute__((address_space(1))) P GP;
+    return (P *)(GP *)pinned(reinterpret_cast<uintptr_t>(p));
+}
 
 // f(std::integral_constant<int, u>) for u = 0 .. N-1: compile-time indices
 // into the register rings, whatever the compiler decides about unrolling.
@@ -130,7 +150,7 @@ struct Tile {
     static constexpr int STAGE = AIMG * 64;            // 16-byte slots per LDS stage
     static constexpr int RING = 2 * STAGE * 16;        // two LDS stages, bytes
     static constexpr int PART = (WK - 1) * BM * BN * 4;     // k-group partial sums
-    static constexpr int PITCH = BN * 2 + 8;           // staged bf16 row, bytes
+    static constexpr int PITCH = BN * 2 + 16;          // staged bf16 row, bytes
     static constexpr int OUTB = BM * PITCH;
     static constexpr int MAIN = cmax(RING, cmax(PART, OUTB));
     static constexpr int SIDE = 2 * BN + BM;           // fp32 ws, bias, xs of the tile
@@ -147,9 +167,26 @@ struct Tile {
 };
 
 template <class T, bool OUT_I32>
-__global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs a)
+__global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args)
 {
     __shared__ uint4 lds[T::LDS / 16];
+
+    MmArgs a;
+    a.xq = pinned_ptr(args.xq);
+    a.xs = pinned_ptr(args.xs);
+    a.wp = pinned_ptr(args.wp);
+    a.ws = pinned_ptr(args.ws);
+    a.bias = pinned_ptr(args.bias);
+    a.out = pinned_ptr(args.out);
+    a.ldq = pinned(args.ldq);
+    a.ldo = pinned(args.ldo);
+    a.M = pinned(args.M);
+    a.N = pinned(args.N);
+    a.K = pinned(args.K);
+    a.kblocks = pinned(args.kblocks);
+    a.nblocks = pinned(args.nblocks);
+    a.vec_store = pinned(args.vec_store);
+    a.vec16 = pinned(args.vec16);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -262,30 +299,40 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs a)
             for (int i = 0; i < T::FM; ++i)
                 x[i][h] = st[(2 * i) * 64 + xslot[h]];
     };
-    auto mma = [&](const v4i (&x)[T::FM][2], const v4i (&b)[T::FN][2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int j = 0; j < T::FN; ++j)
-#pragma unroll
-                for (int i = 0; i < T::FM; ++i)
-                    acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j][h], x[i][h], acc[j][i], 0, 0, 0);
+    // MFMAs number q0 .. q1-1 of a stage, in the order (h, j, i): a wave's 2*FN*FM
+    // MFMAs per stage touch every accumulator twice, FN*FM apart.
+    auto mma = [&](auto q0_c, auto q1_c, const v4i (&x)[T::FM][2], const v4i (&b)[T::FN][2])
+                   __attribute__((always_inline)) {
+        constexpr int q0 = decltype(q0_c)::value, q1 = decltype(q1_c)::value;
+        static_for<q1 - q0>([&](auto Q) __attribute__((always_inline)) {
+            constexpr int q = q0 + decltype(Q)::value;
+            constexpr int h = q / (T::FN * T::FM), j = (q / T::FM) % T::FN, i = q % T::FM;
+            acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j][h], x[i][h], acc[j][i], 0, 0, 0);
+        });
     };
+    constexpr int NMMA = 2 * T::FN * T::FM;            // MFMAs per wave per stage
+    constexpr int PRE = 2;                             // of them issued before the barrier
 
     // Step s. On entry stage s+1 is being written to LDS by every wave, this
     // wave's operands of stage s are in xf[s & 1], token rows of stage s+2
     // sit in staging set (s+2) % NA and the weights of stage s in ring set
-    // s % NB. The step: barrier (stage s+1 visible; every read of stage s
-    // done), read stage s+1's operands, write stage s+2 to the LDS buffer
-    // stage s used, fetch tokens of stage s+2+LT and weights of stage s+LW,
-    // then run stage s's MFMAs.
+    // s % NB. The step: the first MFMAs of stage s (they keep the matrix
+    // core busy across the barrier), barrier (stage s+1 visible; every read
+    // of stage s done), read stage s+1's operands, write stage s+2 to the LDS
+    // buffer stage s used, fetch tokens of stage s+2+LT and weights of stage
+    // s+LW, interleaved one by one with the rest of stage s's MFMAs so that
+    // they issue while the matrix core is busy.
     auto step = [&](auto full, int s, auto u_c) __attribute__((always_inline)) {
         constexpr bool FULL = decltype(full)::value;
         constexpr int u = decltype(u_c)::value;        // s modulo GROUP
+        const bool run = FULL || s * T::WK + wk < a.kblocks;
         if (FULL)
             wait_vm_lgkm0<T::VM>();
         else
             wait_lgkm0();
+        if (run)
+            mma(std::integral_constant<int, 0>{}, std::integral_constant<int, PRE>{}, xf[u & 1],
+                bq[u % T::NB]);
         __builtin_amdgcn_s_barrier();
         if (FULL || s + 1 < S)
             read(s + 1, xf[(u + 1) & 1]);
@@ -295,8 +342,25 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs a)
             load_a(s + 2 + T::LT, ast[(u + 2) % T::NA]);
         if (FULL || s + T::LW < S)
             load_b(s + T::LW, bq[(u + T::LW) % T::NB]);
-        if (FULL || s * T::WK + wk < a.kblocks)
-            mma(xf[u & 1], bq[u % T::NB]);
+        if (run)
+            mma(std::integral_constant<int, PRE>{}, std::integral_constant<int, NMMA>{}, xf[u & 1],
+                bq[u % T::NB]);
+        if (FULL) {
+            // One memory instruction after each MFMA: operand reads first,
+            // then the LDS writes, then the global loads.
+            static_for<2 * T::FM>([&](auto) __attribute__((always_inline)) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+            });
+            static_for<T::LA>([&](auto) __attribute__((always_inline)) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
+            });
+            static_for<T::LPW>([&](auto) __attribute__((always_inline)) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+            });
+        }
         // Keep each step's loads in program order relative to the next
         // step, so the load counter pattern repeats exactly.
         __builtin_amdgcn_sched_barrier(0);
@@ -492,26 +556,38 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs a)
         __builtin_amdgcn_s_barrier();
 
         // ... then write whole rows: consecutive lanes store consecutive
-        // 8-byte pieces, so every store instruction fills complete cache
-        // lines. All LDS reads are issued before the first store.
-        constexpr int QPR = T::BN / 4;                 // 8-byte pieces per row
-        constexpr int PIECES = T::BM * QPR;
-        constexpr int ITER = (PIECES + T::THREADS - 1) / T::THREADS;
-        v2u val[ITER];
+        // pieces, so every store instruction fills complete cache lines. All
+        // LDS reads are issued before the first store. A tile inside the
+        // output with 16-byte aligned rows takes 16-byte pieces with
+        // addresses stepped by a constant; other tiles go piece by piece.
+        constexpr int P16 = T::BN / 8;                 // 16-byte pieces per row
+        constexpr int RPP = T::THREADS / P16;          // rows per pass
+        constexpr int PASSES = (T::BM + RPP - 1) / RPP;
+        if (a.vec16 && m0 + T::BM <= a.M && n0 + T::BN <= a.N) {
+            const int t = threadIdx.x;
+            if (t < RPP * P16) {
+                const int r0 = t / P16, c = t % P16;
+                v4u val[PASSES];
 #pragma unroll
-        for (int it = 0; it < ITER; ++it) {
-            const int p = it * T::THREADS + (int)threadIdx.x;
-            if (PIECES % T::THREADS == 0 || p < PIECES)
-                val[it] = *reinterpret_cast<const v2u *>(tile_lds + (p / QPR) * T::PITCH + (p % QPR) * 8);
+                for (int ps = 0; ps < PASSES; ++ps)
+                    if (T::BM % RPP == 0 || r0 + ps * RPP < T::BM)
+                        val[ps] = *reinterpret_cast<const v4u *>(tile_lds + (r0 + ps * RPP) * T::PITCH + c * 16);
+                uint16_t *o = reinterpret_cast<uint16_t *>(a.out) + (int64_t)(m0 + r0) * a.ldo + n0 + c * 8;
+                const int64_t step = (int64_t)RPP * a.ldo;
+#pragma unroll
+                for (int ps = 0; ps < PASSES; ++ps)
+                    if (T::BM % RPP == 0 || r0 + ps * RPP < T::BM)
+                        *reinterpret_cast<v4u *>(o + ps * step) = val[ps];
+            }
+            return;
         }
-#pragma unroll
-        for (int it = 0; it < ITER; ++it) {
-            const int p = it * T::THREADS + (int)threadIdx.x;
+        constexpr int QPR = T::BN / 4;                 // 8-byte pieces per row
+        for (int p = threadIdx.x; p < T::BM * QPR; p += T::THREADS) {
             const int m = m0 + p / QPR, n = n0 + (p % QPR) * 4;
-            if ((PIECES % T::THREADS != 0 && p >= PIECES) || m >= a.M || n >= a.N)
+            if (m >= a.M || n >= a.N)
                 continue;
+            const v2u v = *reinterpret_cast<const v2u *>(tile_lds + (p / QPR) * T::PITCH + (p % QPR) * 8);
             uint16_t *o = reinterpret_cast<uint16_t *>(a.out) + (int64_t)m * a.ldo + n;
-            const v2u v = val[it];
             if (a.vec_store && n + 3 < a.N) {
                 *reinterpret_cast<v2u *>(o) = v;
             } else {
