@@ -45,6 +45,8 @@
 // read the last valid chunk, which meets zero weights (the prepacked weight
 // is zero beyond K); k-blocks past the end of K are skipped. Every load
 // stays inside its operand; stores are masked.
+#include <algorithm>
+#include <cmath>
 #include <type_traits>
 #include <utility>
 
@@ -70,6 +72,20 @@ __device__ __forceinline__ int xcd_remap(int pid, int tiles)
     const int q = tiles / kXcds, r = tiles % kXcds;
     const int xcd = pid % kXcds, local = pid / kXcds;
     return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+// Logical tile id -> (tm, tn): bands of kBandM M-tiles; inside a band the
+// M index runs fastest. The 32 tiles an XCD runs at once then form a block
+// of at most 4 x 8 output tiles, whose token rows and weight columns its L2
+// holds together, instead of one weight stripe against every token row.
+constexpr int kBandM = 4;
+__device__ __forceinline__ void tile_of(int t, int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    const int band = t / (kBandM * tiles_n);
+    const int r = t - band * kBandM * tiles_n;
+    const int gm = min(kBandM, tiles_m - band * kBandM);   // M-tiles in this band
+    tm = band * kBandM + r % gm;
+    tn = r / gm;
 }
 
 // s_waitcnt lgkmcnt(0) only (vmcnt and expcnt untouched; gfx9 encoding):
@@ -123,16 +139,16 @@ __device__ __forceinline__ void static_for(F &&f)
 constexpr int cgcd(int a, int b) { return b == 0 ? a : cgcd(b, a % b); }
 constexpr int clcm(int a, int b) { return a / cgcd(a, b) * b; }
 
-// BM x BN output tile; WN column groups x WK k-groups of wavefronts; token
-// rows fetched LT stages ahead of their LDS write, weights LW stages ahead
-// of their use.
-template <int BM_, int BN_, int WN_, int WK_, int LT_, int LW_>
+// BM x BN output tile; WM row groups x WN column groups x WK k-groups of
+// wavefronts; token rows fetched LT stages ahead of their LDS write, weights
+// LW stages ahead of their use.
+template <int BM_, int BN_, int WM_, int WN_, int WK_, int LT_, int LW_>
 struct Tile {
-    static constexpr int BM = BM_, BN = BN_, WN = WN_, WK = WK_, LT = LT_, LW = LW_;
-    static constexpr int NW = WN * WK;                 // wavefronts per workgroup
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, WK = WK_, LT = LT_, LW = LW_;
+    static constexpr int NW = WM * WN * WK;            // wavefronts per workgroup
     static constexpr int THREADS = NW * 64;
     static constexpr int MB = BM / 16;                 // 16-row token images per k-block
-    static constexpr int FM = BM / 32;                 // 32x32 MFMA tiles per wave, rows
+    static constexpr int FM = BM / WM / 32;            // 32x32 MFMA tiles per wave, rows
     static constexpr int FN = BN / WN / 32;            // ... and columns
     static constexpr int AIMG = WK * MB;               // token images per stage
     static constexpr int LA = AIMG / NW;               // token loads per wave per stage
@@ -156,13 +172,13 @@ struct Tile {
     static constexpr int SIDE = 2 * BN + BM;           // fp32 ws, bias, xs of the tile
     static constexpr int SIDE_PER_THREAD = (SIDE + THREADS - 1) / THREADS;
     static constexpr int LDS = MAIN + SIDE * 4;
-    static_assert(NW == 4, "four wavefronts per workgroup");
-    static_assert(BM % 32 == 0 && BN % (32 * WN) == 0, "tile/wave mismatch");
+    static_assert(NW == 4 || NW == 8, "four or eight wavefronts per workgroup");
+    static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "tile/wave mismatch");
     static_assert(AIMG % NW == 0, "token loads must split evenly over waves");
     static_assert(LT >= 2 && LW >= LT, "token lead >= 2, weight lead >= token lead");
     static_assert(VM < 64 && (LW + LT) * LPW < 64, "vmcnt range");
     static_assert(LDS <= 160 * 1024, "LDS budget");
-    static_assert(FM * FN * 16 <= 256, "accumulators must fit the AGPR file");
+    static_assert(FM * FN * 16 <= 1024 / NW, "accumulators must leave room for operands");
     static_assert(WK <= 2 && FM % WK == 0, "k-groups split the row tiles evenly");
 };
 
@@ -190,12 +206,12 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wn = wave % T::WN, wk = wave / T::WN;
+    const int wn = wave % T::WN, wm = (wave / T::WN) % T::WM, wk = wave / (T::WN * T::WM);
 
     const int tiles_m = (a.M + T::BM - 1) / T::BM;
     const int tiles_n = (a.N + T::BN - 1) / T::BN;
-    const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
-    const int tn = tile / tiles_m, tm = tile % tiles_m;
+    int tm, tn;
+    tile_of(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
     const int m0 = tm * T::BM, n0 = tn * T::BN;
     const int S = (a.kblocks + T::WK - 1) / T::WK;     // ring stages: WK k-blocks each
     const int klast = a.K - 16;                        // last valid 16-byte k-chunk
@@ -292,7 +308,8 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
     };
     // This wave's token operands of stage t (its k-group's k-block) from LDS.
     auto read = [&](int t, v4i (&x)[T::FM][2]) __attribute__((always_inline)) {
-        const v4i *st = reinterpret_cast<const v4i *>(lds) + (t & 1) * T::STAGE + wk * T::MB * 64;
+        const v4i *st = reinterpret_cast<const v4i *>(lds) + (t & 1) * T::STAGE + wk * T::MB * 64 +
+                        wm * (2 * T::FM) * 64;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -444,7 +461,7 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const v16i &c = acc[j][i];
-                        part[(wn * T::WK + i / FMH) * PW + ((j * FMH + i % FMH) * 4 + q) * 64 + lane] =
+                        part[((wm * T::WN + wn) * T::WK + i / FMH) * PW + ((j * FMH + i % FMH) * 4 + q) * 64 + lane] =
                             v4i{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
                     }
             }
@@ -457,7 +474,7 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
                 for (int j = 0; j < T::FN; ++j)
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        pv[i][j][q] = part[(wn * T::WK + WKI) * PW + ((j * FMH + i) * 4 + q) * 64 + lane];
+                        pv[i][j][q] = part[((wm * T::WN + wn) * T::WK + WKI) * PW + ((j * FMH + i) * 4 + q) * 64 + lane];
         } else {
 #pragma unroll
             for (int i = 0; i < FMH; ++i)
@@ -484,7 +501,7 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
                     const bool full = a.vec_store && n + 3 < a.N;
 #pragma unroll
                     for (int i = 0; i < FMH; ++i) {
-                        const int m = m0 + (i0 + i) * 32 + (lane & 31);
+                        const int m = m0 + wm * (T::BM / T::WM) + (i0 + i) * 32 + (lane & 31);
                         if (m >= a.M)
                             continue;
                         int *o = reinterpret_cast<int *>(a.out) + (int64_t)m * a.ldo + n;
@@ -515,7 +532,7 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
                 w4[j][q] = *reinterpret_cast<const f32x4 *>(side + (wn * T::FN + j) * 32 + q * 8 + (lane >> 5) * 4);
 #pragma unroll
         for (int i = 0; i < FMH; ++i)
-            xr[i] = side[2 * T::BN + (i0 + i) * 32 + (lane & 31)];
+            xr[i] = side[2 * T::BN + wm * (T::BM / T::WM) + (i0 + i) * 32 + (lane & 31)];
         wait_lgkm0();
         __builtin_amdgcn_s_barrier();                  // partials consumed: LDS reusable
 
@@ -526,7 +543,7 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
             constexpr bool B = decltype(with_bias)::value;
 #pragma unroll
             for (int i = 0; i < FMH; ++i) {
-                const int ml = (i0 + i) * 32 + (lane & 31);
+                const int ml = wm * (T::BM / T::WM) + (i0 + i) * 32 + (lane & 31);
 #pragma unroll
                 for (int j = 0; j < T::FN; ++j)
 #pragma unroll
@@ -609,25 +626,30 @@ typedef void (*MmFn)(const MmArgs);
 
 struct TileEntry {
     const char *name;
-    int bm, bn;
+    int bm, bn, threads;
     MmFn bf16, i32;
 };
 
 template <class T>
 constexpr TileEntry entry(const char *name)
 {
-    return TileEntry{name, T::BM, T::BN, scaled_mm_kernel<T, false>, scaled_mm_kernel<T, true>};
+    return TileEntry{name, T::BM, T::BN, T::THREADS, scaled_mm_kernel<T, false>,
+                     scaled_mm_kernel<T, true>};
 }
 
-// BM x BN output tile / WN column groups x WK k-groups of waves / token and
-// weight fetch leads in stages
+// BM x BN output tile / WM row groups x WN column groups x WK k-groups of
+// waves / token and weight fetch leads in stages
 const TileEntry kTiles[] = {
-    entry<Tile<64, 64, 2, 2, 2, 3>>("64x64/n2k2/l23"),
-    entry<Tile<64, 128, 2, 2, 2, 3>>("64x128/n2k2/l23"),
-    entry<Tile<128, 64, 2, 2, 2, 3>>("128x64/n2k2/l23"),
-    entry<Tile<128, 128, 2, 2, 2, 3>>("128x128/n2k2/l23"),
-    entry<Tile<128, 192, 2, 2, 2, 2>>("128x192/n2k2/l22"),
-    entry<Tile<128, 192, 2, 2, 2, 3>>("128x192/n2k2/l23"),
+    entry<Tile<64, 64, 1, 2, 2, 2, 3>>("64x64/m1n2k2/l23"),
+    entry<Tile<64, 128, 1, 2, 2, 2, 3>>("64x128/m1n2k2/l23"),
+    entry<Tile<128, 64, 1, 2, 2, 2, 3>>("128x64/m1n2k2/l23"),
+    entry<Tile<128, 128, 1, 2, 2, 2, 3>>("128x128/m1n2k2/l23"),
+    entry<Tile<128, 192, 1, 2, 2, 2, 3>>("128x192/m1n2k2/l23"),
+    entry<Tile<128, 192, 2, 2, 2, 2, 2>>("128x192/m2n2k2/l22"),
+    entry<Tile<256, 128, 2, 2, 1, 2, 3>>("256x128/m2n2k1/l23"),
+    entry<Tile<256, 192, 2, 2, 1, 2, 3>>("256x192/m2n2k1/l23"),
+    entry<Tile<256, 128, 4, 2, 1, 2, 3>>("256x128/m4n2k1/l23"),
+    entry<Tile<256, 192, 4, 2, 1, 2, 2>>("256x192/m4n2k1/l22"),
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -640,22 +662,26 @@ const char *mm_tile_name(int tile)
     return (tile >= 0 && tile < kNumTiles) ? kTiles[tile].name : "";
 }
 
-// Automatic choice: fewest full-machine rounds of tiles, weighted by how
-// much output each round covers and a penalty for the higher load traffic
-// per op of small tiles.
+// Automatic choice: the smallest modelled time. A tile costs the larger of
+// its MFMA time and the time to stream its operands from L2, plus a fixed
+// cost (prologue and epilogue); tiles run in full-machine rounds of one
+// workgroup per CU. Rates per CU measured on MI355X under full load: about
+// 16000 int8 MFMA ops per ns (the shader clock drops to ~2 GHz) and about 80
+// bytes per ns of L2 reads (the L2s deliver ~20 TB/s in all).
 int mm_tile_auto(int64_t M, int64_t N, int64_t K)
 {
-    (void)K;
-    const int cus = 256;
+    const double cus = 256.0, mfma_ops_per_ns = 16000.0, l2_bytes_per_ns = 80.0, fixed_ns = 3000.0;
     int best = 0;
     double best_cost = 1e300;
     for (int t = 0; t < kNumTiles; ++t) {
         const TileEntry &e = kTiles[t];
         const int64_t tiles = ceil_div(M, e.bm) * ceil_div(N, e.bn);
-        const double rounds = (double)ceil_div(tiles, cus);
-        const double per_op = 1.0 + 48.0 / e.bm + 48.0 / e.bn;
-        const double cost = rounds * e.bm * e.bn * per_op;
-        if (cost < best_cost) {
+        const double rounds = std::ceil((double)tiles / cus);
+        const double kk = (double)round_up(K, 64);
+        const double t_mma = 2.0 * e.bm * e.bn * kk / mfma_ops_per_ns;
+        const double t_l2 = (double)(e.bm + e.bn) * kk / l2_bytes_per_ns;
+        const double cost = rounds * (std::max(t_mma, t_l2) + fixed_ns);
+        if (cost < best_cost * 0.999) {
             best_cost = cost;
             best = t;
         }
@@ -667,7 +693,7 @@ hipError_t launch_scaled_mm(const MmArgs &a, bool out_i32, int tile, hipStream_t
 {
     const TileEntry &e = kTiles[tile];
     const int64_t tiles = ceil_div(a.M, e.bm) * ceil_div(a.N, e.bn);
-    const int threads = 256;
+    const int threads = e.threads;
     hipLaunchKernelGGL(out_i32 ? e.i32 : e.bf16, dim3((unsigned)tiles), dim3(threads), 0, stream, a);
     return hipGetLastError();
 }
