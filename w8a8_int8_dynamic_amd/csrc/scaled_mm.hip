@@ -645,11 +645,8 @@ const TileEntry kTiles[] = {
     entry<Tile<128, 64, 1, 2, 2, 2, 3>>("128x64/m1n2k2/l23"),
     entry<Tile<128, 128, 1, 2, 2, 2, 3>>("128x128/m1n2k2/l23"),
     entry<Tile<128, 192, 1, 2, 2, 2, 3>>("128x192/m1n2k2/l23"),
-    entry<Tile<128, 192, 2, 2, 2, 2, 2>>("128x192/m2n2k2/l22"),
     entry<Tile<256, 128, 2, 2, 1, 2, 3>>("256x128/m2n2k1/l23"),
     entry<Tile<256, 192, 2, 2, 1, 2, 3>>("256x192/m2n2k1/l23"),
-    entry<Tile<256, 128, 4, 2, 1, 2, 3>>("256x128/m4n2k1/l23"),
-    entry<Tile<256, 192, 4, 2, 1, 2, 2>>("256x192/m4n2k1/l22"),
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
