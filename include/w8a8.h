@@ -160,6 +160,41 @@ w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const float *x_
                                   const uint16_t *bias, int64_t M, int64_t N, int64_t K, int mode,
                                   void *out, int64_t ldo, void *stream, int tile);
 
+/*
+ * int8_quant_scaled_mm - the layer's two run-time steps in one call:
+ * int8_quant_per_token of x, then int8_scaled_mm of the result (page "Issue 5
+ * probe ...", "Round two" kernel-path paragraph: a per-token quant followed
+ * by the scaled matmul). Results are bit-identical to calling the two entry
+ * points in sequence.
+ *
+ * Inputs: x bf16 [M, ldx]; w_packed, w_scale, bias as for int8_scaled_mm.
+ * Outputs: the codes xq int8 [M, ldq] and scales x_scale fp32 [M] (written,
+ * as int8_quant_per_token writes them) and out (bf16 or int32 [M, ldo]).
+ * Requirements: those of int8_scaled_mm, plus ldx >= K, x 16-byte aligned
+ * and ldx a multiple of 8; x_scale is required in both output modes.
+ *
+ * When every workgroup of the matmul can be resident at once (true for the
+ * fused-QKV layer at M 512 and smaller), one launch does both steps: each
+ * workgroup quantizes a slice of rows, publishes them through per-row-tile
+ * counters, and waits (bounded) only for the rows of its own tile; should a
+ * wait ever run out, that workgroup quantizes its tile's rows itself, so the
+ * result never depends on scheduling. The counters live in the library's
+ * device memory on each GPU, so calls of this entry point must not overlap
+ * on one device (issue them on one stream, or order the streams).
+ * Otherwise the two steps run as two launches on `stream`.
+ */
+w8a8_status_t int8_quant_scaled_mm(const uint16_t *x, int64_t ldx, int8_t *xq, int64_t ldq,
+                                   float *x_scale, const void *w_packed, const float *w_scale,
+                                   const uint16_t *bias, int64_t M, int64_t N, int64_t K, int mode,
+                                   void *out, int64_t ldo, void *stream);
+
+/* int8_quant_scaled_mm with an explicit tile configuration (or -1). */
+w8a8_status_t int8_quant_scaled_mm_tile(const uint16_t *x, int64_t ldx, int8_t *xq, int64_t ldq,
+                                        float *x_scale, const void *w_packed,
+                                        const float *w_scale, const uint16_t *bias, int64_t M,
+                                        int64_t N, int64_t K, int mode, void *out, int64_t ldo,
+                                        void *stream, int tile);
+
 /* Number of tile configurations, a short name of one ("128x192/n2k2/l23":
  * tile rows x columns / wave column groups and k-groups / token and weight
  * fetch leads in stages),

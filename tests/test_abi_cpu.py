@@ -138,12 +138,34 @@ def test_scaled_mm_validation():
     assert mm(mode=1, xs=None, ws=None, bias=A + 1) in (OK, DEVICE)
 
 
+def qmm(x=A, ldx=64, xq=A, ldq=64, xs=A, wp=A, ws=A, bias=None, M=4, N=16, K=64, mode=0, out=A,
+        ldo=16, tile=-1):
+    return L.int8_quant_scaled_mm_tile(x, ldx, xq, ldq, xs, wp, ws, bias, M, N, K, mode, out, ldo,
+                                       None, tile)
+
+
+def test_quant_scaled_mm_validation():
+    # the matmul's own rules
+    assert qmm(mode=3) == MODE and qmm(tile=-2) == MODE
+    assert qmm(K=72) == SHAPE and qmm(ldq=48) == SHAPE and qmm(ldo=15) == SHAPE
+    assert qmm(xq=None) == NULL and qmm(wp=None) == NULL and qmm(out=None) == NULL
+    assert qmm(xq=A + 8) == ALIGN
+    # the input rows
+    assert qmm(ldx=48) == SHAPE
+    assert qmm(x=None) == NULL
+    assert qmm(x=A + 8) == ALIGN and qmm(ldx=68) == ALIGN
+    # the token scales are written, so they are needed in the int32 mode too
+    assert qmm(mode=1, xs=None, ws=None) == NULL
+    assert qmm(M=0, x=None, xq=None, xs=None, wp=None, ws=None, out=None) == OK
+
+
 def test_no_fallback_without_device():
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert quant() == DEVICE
     assert mm() == DEVICE
+    assert qmm() == DEVICE
     assert L.int8_prepack_weight(A, 16, 64, 64, A, None) == DEVICE
     assert L.w8a8_device_supported(0) == 0
     assert "device" in _lib.last_error()

@@ -303,6 +303,81 @@ def test_workload_full_size(ops, orc, name):
     assert rel < 0.0025
 
 
+# ---------------------------------------------------------------------------
+# Per-token quant and scaled matmul in one call (cooperative single launch
+# where the grid fits the device, two launches otherwise)
+# ---------------------------------------------------------------------------
+QMM_SHAPES = [(1, 48, 64), (37, 45, 80), (130, 200, 336), (257, 300, 1040), (512, 520, 576),
+              (512, 1536, 512)]
+
+
+@pytest.mark.parametrize("M,N,K", QMM_SHAPES)
+@pytest.mark.parametrize("bias", [False, True])
+def test_quant_scaled_mm_matches_two_calls_and_oracle(ops, orc, M, N, K, bias):
+    inp = wl.random_case(M, K, N, 9100 + M + N + K, bias=bias)
+    x = bf16_dev(inp.x_bf16)
+    wq_ref, ws_ref = orc.quant_per_channel(inp.w_f32)
+    packed = ops.prepack_weight(torch.from_numpy(wq_ref).to(DEV))
+    ws = torch.from_numpy(ws_ref).to(DEV)
+    b = bf16_dev(inp.bias_bf16) if bias else None
+    xq_ref, xs_ref = orc.quant_per_token(inp.x_bf16)
+    acc_ref = orc.gemm_i32(xq_ref, wq_ref)
+    ref32 = orc.epilogue_f32(acc_ref, xs_ref, ws_ref, inp.bias_bf16 if bias else None)
+    ref64 = orc.epilogue_f64(acc_ref, xs_ref, ws_ref, inp.bias_bf16 if bias else None)
+    for t in range(ops.tile_count()):
+        for _ in range(2):                     # the second call reuses reset counters
+            out, xq, xs = ops.quant_scaled_mm(x, packed, ws, N, b, tile=t)
+            torch.cuda.synchronize()
+            assert np.array_equal(xs.cpu().numpy(), xs_ref), ops.tile_name(t)
+            assert np.array_equal(xq.cpu().numpy(), xq_ref), ops.tile_name(t)
+            got = bits_np(out)
+            exact = check_out(got, ref32, ref64, f"fused {ops.tile_name(t)} {M}x{N}x{K}")
+            assert exact == 1.0, ops.tile_name(t)
+        acc, _, _ = ops.quant_scaled_mm(x, packed, None, N, out_dtype=torch.int32, tile=t)
+        assert np.array_equal(acc.cpu().numpy(), acc_ref), ops.tile_name(t)
+
+
+def test_quant_scaled_mm_alternating_shapes(ops, orc):
+    """Calls of different shapes back to back on one stream, each checked."""
+    cases = []
+    for i, (M, N, K) in enumerate([(512, 1536, 512), (64, 128, 256), (300, 520, 576)] * 2):
+        inp = wl.random_case(M, K, N, 9300 + i)
+        wq_ref, ws_ref = orc.quant_per_channel(inp.w_f32)
+        packed = ops.prepack_weight(torch.from_numpy(wq_ref).to(DEV))
+        out, _, _ = ops.quant_scaled_mm(bf16_dev(inp.x_bf16), packed,
+                                        torch.from_numpy(ws_ref).to(DEV), N)
+        cases.append((inp, wq_ref, ws_ref, out))
+    torch.cuda.synchronize()
+    for inp, wq_ref, ws_ref, out in cases:
+        xq_ref, xs_ref = orc.quant_per_token(inp.x_bf16)
+        ref32 = orc.epilogue_f32(orc.gemm_i32(xq_ref, wq_ref), xs_ref, ws_ref)
+        assert np.array_equal(bits_np(out), ref32)
+
+
+def test_quant_scaled_mm_reused_buffers(ops, orc):
+    """Back-to-back calls that write new codes into the same xq / xs / out
+    buffers: every call must read the codes of its own input, never a copy
+    left in a cache by the previous call."""
+    M, N, K = 512, 1536, 512
+    inps = [wl.random_case(M, K, N, 9400 + i) for i in range(2)]
+    wq_ref, ws_ref = orc.quant_per_channel(inps[0].w_f32)
+    packed = ops.prepack_weight(torch.from_numpy(wq_ref).to(DEV))
+    ws = torch.from_numpy(ws_ref).to(DEV)
+    xs_dev = [bf16_dev(i.x_bf16) for i in inps]
+    xq = torch.empty((M, K), dtype=torch.int8, device=DEV)
+    xs = torch.empty((M,), dtype=torch.float32, device=DEV)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    refs = []
+    for inp in inps:
+        q_ref, s_ref = orc.quant_per_token(inp.x_bf16)
+        refs.append(orc.epilogue_f32(orc.gemm_i32(q_ref, wq_ref), s_ref, ws_ref))
+    for it in range(8):
+        k = it % 2
+        ops.quant_scaled_mm(xs_dev[k], packed, ws, N, out=out, xq=xq, xs=xs)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_np(out), refs[k]), f"call {it}"
+
+
 def test_linear_keeps_leading_dims(ops, orc):
     from w8a8_int8_dynamic_amd import W8A8Linear
     inp = wl.random_case(2 * 37, 320, 48, 7001)

@@ -34,6 +34,10 @@ SIGNATURES = {
                               _vp]),
     "int8_scaled_mm_tile": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp,
                                    _i64, _vp, _int]),
+    "int8_quant_scaled_mm": (_int, [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                    _int, _vp, _i64, _vp]),
+    "int8_quant_scaled_mm_tile": (_int, [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64,
+                                         _i64, _int, _vp, _i64, _vp, _int]),
     "w8a8_mm_tile_count": (_int, []),
     "w8a8_mm_tile_name": (ctypes.c_char_p, [_int]),
     "w8a8_mm_tile_auto": (_int, [_i64, _i64, _i64]),

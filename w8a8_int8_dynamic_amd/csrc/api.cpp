@@ -178,13 +178,17 @@ W8A8_API w8a8_status_t int8_unpack_weight(const void *w_packed, int64_t N, int64
                     "int8_unpack_weight");
 }
 
-W8A8_API w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const float *x_scale,
-                                           const void *w_packed, const float *w_scale,
-                                           const uint16_t *bias, int64_t M, int64_t N, int64_t K,
-                                           int mode, void *out, int64_t ldo, void *stream,
-                                           int tile)
+namespace {
+
+// Checks the matmul arguments shared by int8_scaled_mm and the fused entry
+// point and fills the kernel arguments. M == 0 passes (the callers return
+// before launching). With need_xs the token scales are required in both
+// output modes (the fused path writes them).
+w8a8_status_t mm_args(const int8_t *xq, int64_t ldq, const float *x_scale, const void *w_packed,
+                      const float *w_scale, const uint16_t *bias, int64_t M, int64_t N, int64_t K,
+                      int mode, void *out, int64_t ldo, int tile, bool need_xs, const char *what,
+                      w8a8::MmArgs &a, int &t)
 {
-    const char *what = "int8_scaled_mm";
     if (mode != W8A8_OUT_BF16 && mode != W8A8_OUT_I32)
         return fail(W8A8_ERR_MODE, "%s: unknown output mode %d", what, mode);
     if (tile < -1 || tile >= w8a8::mm_tile_count())
@@ -195,10 +199,12 @@ W8A8_API w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const 
         return fail(W8A8_ERR_SHAPE, "%s: K must be a multiple of 16 in [16, %d]", what, W8A8_MAX_K);
     if (ldq < K || ldo < N)
         return fail(W8A8_ERR_SHAPE, "%s: leading dimension too small", what);
+    a = w8a8::MmArgs{};
+    t = -1;
     if (M == 0)
         return ok();
     const bool i32 = mode == W8A8_OUT_I32;
-    if (!xq || !w_packed || !out || (!i32 && (!x_scale || !w_scale)))
+    if (!xq || !w_packed || !out || (!i32 && !w_scale) || ((need_xs || !i32) && !x_scale))
         return fail(W8A8_ERR_NULL, "%s: NULL tensor pointer", what);
     if (!aligned(xq, 16) || ldq % 16 != 0 || !aligned(w_packed, 16))
         return fail(W8A8_ERR_ALIGN, "%s: xq/w_packed must be 16-byte aligned, ldq a multiple of 16",
@@ -206,16 +212,11 @@ W8A8_API w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const 
     const uintptr_t esz = i32 ? 4 : 2;
     if (!aligned(out, esz))
         return fail(W8A8_ERR_ALIGN, "%s: out must be aligned to its element size", what);
-    if (!i32 && (!aligned(x_scale, 4) || !aligned(w_scale, 4) || (bias && !aligned(bias, 2))))
+    if ((x_scale && !aligned(x_scale, 4)) || (!i32 && (!aligned(w_scale, 4) || (bias && !aligned(bias, 2)))))
         return fail(W8A8_ERR_ALIGN, "%s: scales/bias misaligned", what);
-    const int t = tile >= 0 ? tile : w8a8::mm_tile_auto(M, N, K);
-    w8a8_status_t st = check_device();
-    if (st != W8A8_OK)
-        return st;
-
-    w8a8::MmArgs a;
+    t = tile >= 0 ? tile : w8a8::mm_tile_auto(M, N, K);
     a.xq = xq;
-    a.xs = i32 ? nullptr : x_scale;
+    a.xs = (i32 && !need_xs) ? nullptr : x_scale;
     a.wp = reinterpret_cast<const int8_t *>(w_packed);
     a.ws = i32 ? nullptr : w_scale;
     a.bias = i32 ? nullptr : bias;
@@ -232,7 +233,83 @@ W8A8_API w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const 
     const uintptr_t vw = 4 * esz;
     a.vec_store = aligned(out, vw) && ((uint64_t)ldo * esz) % vw == 0;
     a.vec16 = aligned(out, 16) && ((uint64_t)ldo * esz) % 16 == 0;
-    return launched(w8a8::launch_scaled_mm(a, i32, t, reinterpret_cast<hipStream_t>(stream)), what);
+    a.x = nullptr;
+    return ok();
+}
+
+}  // namespace
+
+W8A8_API w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const float *x_scale,
+                                           const void *w_packed, const float *w_scale,
+                                           const uint16_t *bias, int64_t M, int64_t N, int64_t K,
+                                           int mode, void *out, int64_t ldo, void *stream,
+                                           int tile)
+{
+    const char *what = "int8_scaled_mm";
+    w8a8::MmArgs a;
+    int t;
+    w8a8_status_t st = mm_args(xq, ldq, x_scale, w_packed, w_scale, bias, M, N, K, mode, out, ldo,
+                               tile, false, what, a, t);
+    if (st != W8A8_OK || M == 0)
+        return st;
+    st = check_device();
+    if (st != W8A8_OK)
+        return st;
+    return launched(w8a8::launch_scaled_mm(a, mode == W8A8_OUT_I32, t,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                    what);
+}
+
+W8A8_API w8a8_status_t int8_quant_scaled_mm_tile(const uint16_t *x, int64_t ldx, int8_t *xq,
+                                                 int64_t ldq, float *x_scale,
+                                                 const void *w_packed, const float *w_scale,
+                                                 const uint16_t *bias, int64_t M, int64_t N,
+                                                 int64_t K, int mode, void *out, int64_t ldo,
+                                                 void *stream, int tile)
+{
+    const char *what = "int8_quant_scaled_mm";
+    w8a8::MmArgs a;
+    int t;
+    w8a8_status_t st = mm_args(xq, ldq, x_scale, w_packed, w_scale, bias, M, N, K, mode, out, ldo,
+                               tile, true, what, a, t);
+    if (st != W8A8_OK)
+        return st;
+    if (ldx < K)
+        return fail(W8A8_ERR_SHAPE, "%s: ldx smaller than K", what);
+    if (M == 0)
+        return ok();
+    if (!x)
+        return fail(W8A8_ERR_NULL, "%s: NULL tensor pointer", what);
+    if (!aligned(x, 16) || ldx % 8 != 0)
+        return fail(W8A8_ERR_ALIGN, "%s: x must be 16-byte aligned with ldx a multiple of 8", what);
+    st = check_device();
+    if (st != W8A8_OK)
+        return st;
+    const bool i32 = mode == W8A8_OUT_I32;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    a.x = x;
+    a.ldx = ldx;
+    hipError_t err = w8a8::launch_quant_scaled_mm(a, i32, t, s);
+    if (err != hipErrorNotSupported)
+        return launched(err, what);
+    // The grid cannot be resident all at once: run the two steps as two
+    // launches on the same stream.
+    (void)hipGetLastError();
+    a.x = nullptr;
+    err = w8a8::launch_quant_rows(x, false, M, K, ldx, xq, ldq, x_scale, s);
+    if (err != hipSuccess)
+        return launched(err, what);
+    return launched(w8a8::launch_scaled_mm(a, i32, t, s), what);
+}
+
+W8A8_API w8a8_status_t int8_quant_scaled_mm(const uint16_t *x, int64_t ldx, int8_t *xq,
+                                            int64_t ldq, float *x_scale, const void *w_packed,
+                                            const float *w_scale, const uint16_t *bias, int64_t M,
+                                            int64_t N, int64_t K, int mode, void *out,
+                                            int64_t ldo, void *stream)
+{
+    return int8_quant_scaled_mm_tile(x, ldx, xq, ldq, x_scale, w_packed, w_scale, bias, M, N, K,
+                                     mode, out, ldo, stream, -1);
 }
 
 W8A8_API w8a8_status_t int8_scaled_mm(const int8_t *xq, int64_t ldq, const float *x_scale,

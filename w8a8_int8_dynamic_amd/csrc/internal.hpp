@@ -41,11 +41,21 @@ struct MmArgs {
     int nblocks;     // round_up(N, 16) / 16: fragments along N in the packed weight
     int vec_store;   // 1 when out rows allow stores of 4 consecutive elements
     int vec16;       // 1 when out rows start on 16-byte boundaries
+    // Fused quant: when x is set, the launch first quantizes x [M, ldx] (bf16)
+    // into xq / xs, rows_per_wg rows per workgroup, then runs the matmul.
+    const uint16_t *x;
+    int64_t ldx;
+    int rows_per_wg;
+    unsigned epoch;  // this launch's number on its device, never 0
 };
 
 int mm_tile_count();
 const char *mm_tile_name(int tile);
 int mm_tile_auto(int64_t M, int64_t N, int64_t K);
 hipError_t launch_scaled_mm(const MmArgs &a, bool out_i32, int tile, hipStream_t stream);
+// Fused quant + matmul in one launch. Returns hipErrorNotSupported (nothing
+// launched) when the shape's workgroups cannot all be resident at once; the
+// caller then runs the two steps as separate launches.
+hipError_t launch_quant_scaled_mm(MmArgs a, bool out_i32, int tile, hipStream_t stream);
 
 }  // namespace w8a8

@@ -28,138 +28,12 @@
 // Every tail (K not a multiple of the chunk width, rows beyond the last)
 // is masked element by element.
 #include "internal.hpp"
+#include "quant_rule.hpp"
 
 namespace w8a8 {
 namespace {
 
-typedef unsigned int u32;
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
-typedef unsigned v2u __attribute__((ext_vector_type(2)));
-
-// Wavefront max of non-negative values carried as unsigned bit patterns.
-__device__ __forceinline__ u32 wave_max(u32 v)
-{
-    // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror:
-    // afterwards every lane of a 16-lane row holds the row's max.
-    v = max(v, (u32)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
-    v = max(v, (u32)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
-    v = max(v, (u32)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));
-    v = max(v, (u32)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));
-    u32 r0 = (u32)__builtin_amdgcn_readlane((int)v, 0);
-    u32 r1 = (u32)__builtin_amdgcn_readlane((int)v, 16);
-    u32 r2 = (u32)__builtin_amdgcn_readlane((int)v, 32);
-    u32 r3 = (u32)__builtin_amdgcn_readlane((int)v, 48);
-    return max(max(r0, r1), max(r2, r3));
-}
-
-template <bool F32>
-struct Elem {
-    static constexpr int VEC = F32 ? 4 : 8;       // elements per 16-byte chunk
-    static constexpr int BYTES = F32 ? 4 : 2;
-};
-
-// Largest |x| bit pattern in one chunk.
-template <bool F32>
-__device__ __forceinline__ u32 chunk_absmax(const uint4 &v)
-{
-    const u32 d[4] = {v.x, v.y, v.z, v.w};
-    u32 m = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (F32) {
-            m = max(m, d[i] & 0x7fffffffu);
-        } else {
-            m = max(m, d[i] & 0x7fffu);
-            m = max(m, (d[i] >> 16) & 0x7fffu);
-        }
-    }
-    return m;
-}
-
-__device__ __forceinline__ u32 code(float f, float inv)
-{
-    float t = __builtin_rintf(f * inv);
-    t = fminf(fmaxf(t, -127.0f), 127.0f);
-    return (u32)((int)t) & 0xffu;
-}
-
-// Codes of one chunk: bf16 -> 8 codes in (lo, hi); fp32 -> 4 codes in lo.
-template <bool F32>
-__device__ __forceinline__ void chunk_codes(const uint4 &v, float inv, u32 &lo, u32 &hi)
-{
-    const u32 d[4] = {v.x, v.y, v.z, v.w};
-    if (F32) {
-        lo = code(__uint_as_float(d[0]), inv) | code(__uint_as_float(d[1]), inv) << 8 |
-             code(__uint_as_float(d[2]), inv) << 16 | code(__uint_as_float(d[3]), inv) << 24;
-        hi = 0;
-    } else {
-        u32 c[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            c[2 * i] = code(__uint_as_float(d[i] << 16), inv);
-            c[2 * i + 1] = code(__uint_as_float(d[i] & 0xffff0000u), inv);
-        }
-        lo = c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24;
-        hi = c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24;
-    }
-}
-
-// Load chunk starting at element e of a row (row pointer as bytes). STREAM
-// marks the data as read once (nontemporal: it is not kept in the caches),
-// which the single-pass kernel uses; measured on MI355X this raises the
-// quant's HBM throughput by about 14 % on 300 MB passes.
-template <bool F32, bool STREAM = false>
-__device__ __forceinline__ uint4 load_chunk(const char *row, int64_t e, int K)
-{
-    constexpr int VEC = Elem<F32>::VEC;
-    constexpr int B = Elem<F32>::BYTES;
-    if (e + VEC <= K) {
-        if (STREAM) {
-            const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(row + e * B));
-            return make_uint4(t[0], t[1], t[2], t[3]);
-        }
-        return *reinterpret_cast<const uint4 *>(row + e * B);
-    }
-    u32 w[4] = {0, 0, 0, 0};
-    for (int j = 0; j < VEC; ++j) {
-        if (e + j < K) {
-            if (F32)
-                w[j] = reinterpret_cast<const u32 *>(row)[e + j];
-            else
-                w[j >> 1] |= (u32)reinterpret_cast<const uint16_t *>(row)[e + j] << (16 * (j & 1));
-        }
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-template <bool F32>
-__device__ __forceinline__ void store_codes(int8_t *qrow, int64_t e, int K, u32 lo, u32 hi)
-{
-    constexpr int VEC = Elem<F32>::VEC;
-    if (e + VEC <= K) {
-        // The codes are not read again by this pass: stream them out.
-        if (F32)
-            __builtin_nontemporal_store(lo, reinterpret_cast<u32 *>(qrow + e));
-        else
-            __builtin_nontemporal_store(v2u{lo, hi}, reinterpret_cast<v2u *>(qrow + e));
-        return;
-    }
-    for (int j = 0; j < VEC; ++j)
-        if (e + j < K)
-            qrow[e + j] = (int8_t)((j < 4 ? lo >> (8 * j) : hi >> (8 * (j - 4))) & 0xffu);
-}
-
-__device__ __forceinline__ void scale_of(u32 m, bool f32, float &s, float &inv)
-{
-    const float a = __uint_as_float(f32 ? m : m << 16);
-    if (a < 0x1p-100f) {
-        s = 0.0f;
-        inv = 0.0f;                      // x * 0 -> code 0 for every element
-    } else {
-        s = a / 127.0f;                  // correctly rounded fp32 divide
-        inv = 127.0f / a;
-    }
-}
+using namespace quant_rule;
 
 // Register-resident kernel: CH chunks per lane, WPR waves per row, 4 waves per block.
 template <bool F32, int CH, int WPR>

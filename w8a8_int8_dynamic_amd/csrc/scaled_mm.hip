@@ -46,11 +46,13 @@
 // is zero beyond K); k-blocks past the end of K are skipped. Every load
 // stays inside its operand; stores are masked.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <type_traits>
 #include <utility>
 
 #include "internal.hpp"
+#include "quant_rule.hpp"
 
 namespace w8a8 {
 namespace {
@@ -64,6 +66,20 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kXcds = 8;
+
+// Fused quant + matmul: workgroup w of a launch stores the launch's epoch
+// (a per-device launch number, never 0) in g_fused_flag[w] once its rows
+// are quantized. A consumer accepts a tile when every producer of its rows
+// shows the current epoch, so nothing is ever reset. Flags are plain
+// coherent stores and loads, one word per producer: no read-modify-write
+// on a shared word, which would serialize at the memory side.
+constexpr int kMaxFusedWgs = 16384;
+__device__ unsigned g_fused_flag[kMaxFusedWgs];
+// Bound on the polls for a tile's rows (each ~1 us; a few ms in all): far
+// beyond any real wait. Past it a workgroup quantizes its tile's rows
+// itself, writing the same bytes as their producers, so no wave can spin
+// forever and launches that overlap on one device stay correct.
+constexpr int kSpinLimit = 1 << 12;
 
 // Physical workgroup id -> logical tile id such that each XCD (which takes
 // ids pid % 8 round-robin) receives one contiguous run of logical ids.
@@ -168,10 +184,12 @@ struct Tile {
     static constexpr int PART = (WK - 1) * BM * BN * 4;     // k-group partial sums
     static constexpr int PITCH = BN * 2 + 16;          // staged bf16 row, bytes
     static constexpr int OUTB = BM * PITCH;
-    static constexpr int MAIN = cmax(RING, cmax(PART, OUTB));
+    static constexpr int TILE_OFF = cmax(RING, PART);  // bf16 tile after ring / partials
+    static constexpr int MAIN = TILE_OFF + OUTB;
     static constexpr int SIDE = 2 * BN + BM;           // fp32 ws, bias, xs of the tile
     static constexpr int SIDE_PER_THREAD = (SIDE + THREADS - 1) / THREADS;
-    static constexpr int LDS = MAIN + SIDE * 4;
+    static constexpr int FLAG = MAIN + SIDE * 4;        // one word: fused-path decision
+    static constexpr int LDS = FLAG + 16;
     static_assert(NW == 4 || NW == 8, "four or eight wavefronts per workgroup");
     static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "tile/wave mismatch");
     static_assert(AIMG % NW == 0, "token loads must split evenly over waves");
@@ -182,7 +200,7 @@ struct Tile {
     static_assert(WK <= 2 && FM % WK == 0, "k-groups split the row tiles evenly");
 };
 
-template <class T, bool OUT_I32>
+template <class T, bool OUT_I32, bool FUSED>
 __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args)
 {
     __shared__ uint4 lds[T::LDS / 16];
@@ -203,6 +221,12 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
     a.nblocks = pinned(args.nblocks);
     a.vec_store = pinned(args.vec_store);
     a.vec16 = pinned(args.vec16);
+    if (FUSED) {
+        a.x = pinned_ptr(args.x);
+        a.ldx = pinned(args.ldx);
+        a.rows_per_wg = pinned(args.rows_per_wg);
+        a.epoch = pinned(args.epoch);
+    }
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -247,28 +271,6 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
     for (int h = 0; h < 2; ++h) {
         const int r16 = lane & 15, c = 2 * h + (lane >> 5);
         xslot[h] = ((lane >> 4) & 1) * 64 + 4 * r16 + (c ^ tok_swz(r16));
-    }
-
-    // Scales (and bias) of the tile, fetched now into a couple of registers
-    // per thread and parked in LDS for the epilogue, so that their latency
-    // hides behind the K loop: entries [0, BN) ws, [BN, 2BN) bias as fp32
-    // (zero without bias), [2BN, 2BN+BM) xs; rows/channels past M/N repeat
-    // the last valid one.
-    float side_v[T::SIDE_PER_THREAD];
-    if (!OUT_I32) {
-#pragma unroll
-        for (int u = 0; u < T::SIDE_PER_THREAD; ++u) {
-            const int p = u * T::THREADS + (int)threadIdx.x;
-            float v = 0.0f;
-            if (p < T::BN)
-                v = a.ws[min(n0 + p, a.N - 1)];
-            else if (p < 2 * T::BN) {
-                if (a.bias)
-                    v = __uint_as_float((unsigned)a.bias[min(n0 + p - T::BN, a.N - 1)] << 16);
-            } else if (p < T::SIDE)
-                v = a.xs[min(m0 + p - 2 * T::BN, a.M - 1)];
-            side_v[u] = v;
-        }
     }
 
     v16i acc[T::FN][T::FM];
@@ -385,6 +387,183 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
     using Full = std::integral_constant<bool, true>;
     using Part = std::integral_constant<bool, false>;
 
+    if (FUSED) {
+        // Fused quant, producer side: this workgroup quantizes rows
+        // [r0, r1) of x with the rule of int8_quant_per_token, then
+        // publishes them for its M-tile (rows_per_wg divides BM, so the rows
+        // belong to one tile). A row up to QCH * 8 * THREADS elements long is
+        // held in registers (one read); longer rows take an absmax pass and
+        // a codes pass that re-reads the row from L2.
+        using namespace quant_rule;
+        constexpr int QCH = 8;
+        const int r0 = (int)blockIdx.x * a.rows_per_wg;
+        const int r1 = min(r0 + a.rows_per_wg, a.M);
+        u32 *red = reinterpret_cast<u32 *>(lds);
+        // A word no other phase writes: every wave reads it after the
+        // barrier below while others may already be filling the ring.
+        u32 *flag = reinterpret_cast<u32 *>(reinterpret_cast<char *>(lds) + T::FLAG);
+        // Codes and scales are written with agent-scope (relaxed atomic)
+        // stores: they are coherent across the XCDs once complete, so no
+        // write-back of this XCD's L2 is needed before they are published.
+        // K is a multiple of 16, so every 8-code chunk is whole.
+        auto put_codes = [&](int8_t *qrow, int e, u32 lo, u32 hi) __attribute__((always_inline)) {
+            __hip_atomic_store(reinterpret_cast<uint64_t *>(qrow + e), (uint64_t)hi << 32 | lo,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        // One row group (1 or 2 rows) held in registers: every load of the
+        // group is issued before the reductions.
+        auto rows_in_regs = [&](auto nr_c, int r) __attribute__((always_inline)) {
+            constexpr int NR = decltype(nr_c)::value;
+            constexpr int CH = QCH / NR;
+            uint4 v[NR][CH];
+            u32 mx[NR];
+#pragma unroll
+            for (int k = 0; k < NR; ++k) {
+                const char *xrow = reinterpret_cast<const char *>(a.x + (int64_t)(r + k) * a.ldx);
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    const int e = (c * T::THREADS + (int)threadIdx.x) * 8;
+                    v[k][c] = e < a.K ? load_chunk<false>(xrow, e, a.K) : make_uint4(0, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < NR; ++k) {
+                mx[k] = 0;
+#pragma unroll
+                for (int c = 0; c < CH; ++c)
+                    mx[k] = max(mx[k], chunk_absmax<false>(v[k][c]));
+                mx[k] = wave_max(mx[k]);
+                if (lane == 0)
+                    red[k * T::NW + wave] = mx[k];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < NR; ++k)
+#pragma unroll
+                for (int w = 0; w < T::NW; ++w)
+                    mx[k] = max(mx[k], red[k * T::NW + w]);
+            __syncthreads();                           // red is rewritten by the next group
+#pragma unroll
+            for (int k = 0; k < NR; ++k) {
+                float sc, inv;
+                scale_of(mx[k], false, sc, inv);
+                int8_t *qrow = const_cast<int8_t *>(a.xq) + (int64_t)(r + k) * a.ldq;
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    const int e = (c * T::THREADS + (int)threadIdx.x) * 8;
+                    if (e < a.K) {
+                        u32 lo, hi;
+                        chunk_codes<false>(v[k][c], inv, lo, hi);
+                        put_codes(qrow, e, lo, hi);
+                    }
+                }
+                if (threadIdx.x == 0)
+                    __hip_atomic_store(const_cast<float *>(a.xs) + r + k, sc, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+        };
+        // A row too long for registers: an absmax pass, then a codes pass
+        // that re-reads the row from L2.
+        auto row_looped = [&](int r) __attribute__((always_inline)) {
+            const char *xrow = reinterpret_cast<const char *>(a.x + (int64_t)r * a.ldx);
+            int8_t *qrow = const_cast<int8_t *>(a.xq) + (int64_t)r * a.ldq;
+            u32 mx = 0;
+            for (int e = (int)threadIdx.x * 8; e < a.K; e += T::THREADS * 8)
+                mx = max(mx, chunk_absmax<false>(load_chunk<false>(xrow, e, a.K)));
+            mx = wave_max(mx);
+            if (lane == 0)
+                red[wave] = mx;
+            __syncthreads();
+#pragma unroll
+            for (int w = 0; w < T::NW; ++w)
+                mx = max(mx, red[w]);
+            __syncthreads();
+            float sc, inv;
+            scale_of(mx, false, sc, inv);
+            for (int e = (int)threadIdx.x * 8; e < a.K; e += T::THREADS * 8) {
+                u32 lo, hi;
+                chunk_codes<false>(load_chunk<false>(xrow, e, a.K), inv, lo, hi);
+                put_codes(qrow, e, lo, hi);
+            }
+            if (threadIdx.x == 0)
+                __hip_atomic_store(const_cast<float *>(a.xs) + r, sc, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        };
+        auto quantize_rows = [&](int ra, int rb) __attribute__((always_inline)) {
+            int r = ra;
+            if (a.K <= (QCH / 2) * 8 * T::THREADS)
+                for (; r + 2 <= rb; r += 2)
+                    rows_in_regs(std::integral_constant<int, 2>{}, r);
+            for (; r < rb; ++r) {
+                if (a.K <= QCH * 8 * T::THREADS)
+                    rows_in_regs(std::integral_constant<int, 1>{}, r);
+                else
+                    row_looped(r);
+            }
+        };
+        quantize_rows(r0, r1);
+        // Every wave's stores have completed; then one thread raises this
+        // workgroup's flag.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0 && r0 < r1)
+            __hip_atomic_store(&g_fused_flag[blockIdx.x], a.epoch, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+
+        // Consumer side: wait until every producer of this tile's rows has
+        // published. No cache of this CU or XCD can hold an older copy of
+        // those rows: the caches start each launch clean, and no workgroup
+        // reads a tile's rows before this wait. The wait is bounded: should
+        // it ever run out (a device that does not run every workgroup of the
+        // grid at once), this workgroup quantizes its tile's rows itself,
+        // writing the same bytes the producers write, and goes on.
+        const int rows = min(T::BM, a.M - m0);
+        const int producers = (rows + a.rows_per_wg - 1) / a.rows_per_wg;
+        const int p0 = m0 / a.rows_per_wg;             // first producer of this tile
+        if (wave == 0) {
+            int it = 0;
+            for (; it < kSpinLimit; ++it) {
+                bool ready = true;
+                for (int i = lane; i < producers; i += 64)
+                    ready &= __hip_atomic_load(&g_fused_flag[p0 + i], __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
+                if (__all(ready))
+                    break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+            if (lane == 0)
+                flag[0] = it == kSpinLimit;
+        }
+        __syncthreads();
+        if (flag[0]) {
+            quantize_rows(m0, m0 + rows);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+    }
+
+    // Scales (and bias) of the tile, fetched now into a couple of registers
+    // per thread and parked in LDS for the epilogue, so that their latency
+    // hides behind the K loop: entries [0, BN) ws, [BN, 2BN) bias as fp32
+    // (zero without bias), [2BN, 2BN+BM) xs; rows/channels past M/N repeat
+    // the last valid one.
+    float side_v[T::SIDE_PER_THREAD];
+    if (!OUT_I32) {
+#pragma unroll
+        for (int u = 0; u < T::SIDE_PER_THREAD; ++u) {
+            const int p = u * T::THREADS + (int)threadIdx.x;
+            float v = 0.0f;
+            if (p < T::BN)
+                v = a.ws[min(n0 + p, a.N - 1)];
+            else if (p < 2 * T::BN) {
+                if (a.bias)
+                    v = __uint_as_float((unsigned)a.bias[min(n0 + p - T::BN, a.N - 1)] << 16);
+            } else if (p < T::SIDE)
+                v = a.xs[min(m0 + p - 2 * T::BN, a.M - 1)];
+            side_v[u] = v;
+        }
+    }
+
     // Prologue: stages 0 and 1 into LDS, stage 0's operands into xf[0], and
     // the loads that steps -LT .. -1 would have issued. Every load is issued
     // even when its stage does not exist, so the load counter state at the
@@ -446,12 +625,13 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
         wait_lgkm0();
         __builtin_amdgcn_s_barrier();                  // every wave is done with the ring
 
-        // The other k-group's partial sums of this wave's rows, one 16-byte
-        // slot per (j, i % FMH, q, lane) of each (column group, owner).
-        v4i pv[FMH][T::FN][4];
+        // Hand over the partial sums of the other k-group's rows: one 16-byte
+        // slot per (j, i % FMH, q, lane) of each (row group, column group,
+        // owner k-group).
+        v4i *part = reinterpret_cast<v4i *>(lds);
+        constexpr int PW = T::FN * FMH * 4 * 64;
+        const int pbase = ((wm * T::WN + wn) * T::WK + WKI) * PW;
         if (T::WK > 1) {
-            v4i *part = reinterpret_cast<v4i *>(lds);
-            constexpr int PW = T::FN * FMH * 4 * 64;
 #pragma unroll
             for (int i = 0; i < T::FM; ++i) {
                 if (i / FMH == WKI)
@@ -467,93 +647,80 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
             }
             wait_lgkm0();
             __builtin_amdgcn_s_barrier();
-            // All reads first, one wait: they are independent.
-#pragma unroll
-            for (int i = 0; i < FMH; ++i)
-#pragma unroll
-                for (int j = 0; j < T::FN; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        pv[i][j][q] = part[((wm * T::WN + wn) * T::WK + WKI) * PW + ((j * FMH + i) * 4 + q) * 64 + lane];
-        } else {
-#pragma unroll
-            for (int i = 0; i < FMH; ++i)
-#pragma unroll
-                for (int j = 0; j < T::FN; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        pv[i][j][q] = v4i{};
         }
-        // Final int32 sums of this wave's outputs.
-        auto sum = [&](int i, int j, int q, int r) __attribute__((always_inline)) {
-            return acc[j][i0 + i][4 * q + r] + pv[i][j][q][r];
-        };
-
-        if (OUT_I32) {
-            // Debug mode: raw accumulators straight from registers.
+        // The other k-group's partial sums of row tile i0+i of this wave, read
+        // one row tile at a time (they are independent loads, issued together).
+        auto partials = [&](int i, v4i (&pv)[T::FN][4]) __attribute__((always_inline)) {
 #pragma unroll
             for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = n0 + (wn * T::FN + j) * 32 + q * 8 + (lane >> 5) * 4;
-                    if (n >= a.N)
-                        continue;
-                    const bool full = a.vec_store && n + 3 < a.N;
+                for (int q = 0; q < 4; ++q)
+                    pv[j][q] = T::WK > 1 ? part[pbase + ((j * FMH + i) * 4 + q) * 64 + lane] : v4i{};
+        };
+
+        if (OUT_I32) {
+            // Debug mode: raw int32 sums straight from registers.
 #pragma unroll
-                    for (int i = 0; i < FMH; ++i) {
-                        const int m = m0 + wm * (T::BM / T::WM) + (i0 + i) * 32 + (lane & 31);
-                        if (m >= a.M)
+            for (int i = 0; i < FMH; ++i) {
+                v4i pv[T::FN][4];
+                partials(i, pv);
+                const int m = m0 + wm * (T::BM / T::WM) + (i0 + i) * 32 + (lane & 31);
+                if (m >= a.M)
+                    continue;
+#pragma unroll
+                for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int n = n0 + (wn * T::FN + j) * 32 + q * 8 + (lane >> 5) * 4;
+                        if (n >= a.N)
                             continue;
+                        const v16i &c = acc[j][i0 + i];
+                        const v4i v = v4i{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]} + pv[j][q];
                         int *o = reinterpret_cast<int *>(a.out) + (int64_t)m * a.ldo + n;
-                        if (full) {
-                            *reinterpret_cast<v4i *>(o) = v4i{sum(i, j, q, 0), sum(i, j, q, 1),
-                                                              sum(i, j, q, 2), sum(i, j, q, 3)};
+                        if (a.vec_store && n + 3 < a.N) {
+                            *reinterpret_cast<v4i *>(o) = v;
                         } else {
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
                                 if (n + r < a.N)
-                                    o[r] = sum(i, j, q, r);
+                                    o[r] = v[r];
                         }
                     }
-                }
+            }
             return;
         }
 
-        // bf16 output. Scales of this wave's columns and rows from LDS (all
-        // reads issued together), then the epilogue's fixed order per output:
-        // acc * xs, then * ws, then + bias, each step rounded to fp32, and a
-        // round-to-nearest-even pair conversion to bf16.
+        // bf16 output. Scales of this wave's columns and rows from LDS, then
+        // the epilogue's fixed order per output: acc * xs, then * ws, then
+        // + bias, each step rounded to fp32, and a round-to-nearest-even pair
+        // conversion to bf16. The BM x BN bf16 tile is staged in LDS (its own
+        // region, row pitch BN*2+16 bytes) ...
         f32x4 w4[T::FN][4];
-        float xr[FMH];
 #pragma unroll
         for (int j = 0; j < T::FN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 w4[j][q] = *reinterpret_cast<const f32x4 *>(side + (wn * T::FN + j) * 32 + q * 8 + (lane >> 5) * 4);
-#pragma unroll
-        for (int i = 0; i < FMH; ++i)
-            xr[i] = side[2 * T::BN + wm * (T::BM / T::WM) + (i0 + i) * 32 + (lane & 31)];
-        wait_lgkm0();
-        __builtin_amdgcn_s_barrier();                  // partials consumed: LDS reusable
-
-        // Stage the BM x BN bf16 tile in LDS (row pitch BN*2+8 bytes keeps
-        // the 8-byte writes of 32 rows on distinct banks) ...
-        char *tile_lds = reinterpret_cast<char *>(lds);
+        char *tile_lds = reinterpret_cast<char *>(lds) + T::TILE_OFF;
         auto scale = [&](auto with_bias) __attribute__((always_inline)) {
             constexpr bool B = decltype(with_bias)::value;
 #pragma unroll
             for (int i = 0; i < FMH; ++i) {
+                v4i pv[T::FN][4];
+                partials(i, pv);
                 const int ml = wm * (T::BM / T::WM) + (i0 + i) * 32 + (lane & 31);
+                const float xr = side[2 * T::BN + ml];
 #pragma unroll
                 for (int j = 0; j < T::FN; ++j)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int nl = (wn * T::FN + j) * 32 + q * 8 + (lane >> 5) * 4;
                         const f32x4 b4 = B ? *reinterpret_cast<const f32x4 *>(side + T::BN + nl) : f32x4{};
+                        const v16i &c = acc[j][i0 + i];
                         float t[4];
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            t[r] = (float)sum(i, j, q, r) * xr[i];
+                            t[r] = (float)(c[4 * q + r] + pv[j][q][r]) * xr;
                             t[r] = t[r] * w4[j][q][r];
                             if (B)
                                 t[r] = t[r] + b4[r];
@@ -627,14 +794,15 @@ typedef void (*MmFn)(const MmArgs);
 struct TileEntry {
     const char *name;
     int bm, bn, threads;
-    MmFn bf16, i32;
+    MmFn bf16, i32, bf16_fused, i32_fused;
 };
 
 template <class T>
 constexpr TileEntry entry(const char *name)
 {
-    return TileEntry{name, T::BM, T::BN, T::THREADS, scaled_mm_kernel<T, false>,
-                     scaled_mm_kernel<T, true>};
+    return TileEntry{name, T::BM, T::BN, T::THREADS, scaled_mm_kernel<T, false, false>,
+                     scaled_mm_kernel<T, true, false>, scaled_mm_kernel<T, false, true>,
+                     scaled_mm_kernel<T, true, true>};
 }
 
 // BM x BN output tile / WM row groups x WN column groups x WK k-groups of
@@ -692,6 +860,50 @@ hipError_t launch_scaled_mm(const MmArgs &a, bool out_i32, int tile, hipStream_t
     const int64_t tiles = ceil_div(a.M, e.bm) * ceil_div(a.N, e.bn);
     const int threads = e.threads;
     hipLaunchKernelGGL(out_i32 ? e.i32 : e.bf16, dim3((unsigned)tiles), dim3(threads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_scaled_mm(MmArgs a, bool out_i32, int tile, hipStream_t stream)
+{
+    const TileEntry &e = kTiles[tile];
+    const int64_t tiles_m = ceil_div(a.M, e.bm);
+    const int64_t tiles = tiles_m * ceil_div(a.N, e.bn);
+    if (tiles > kMaxFusedWgs)
+        return hipErrorNotSupported;
+    MmFn fn = out_i32 ? e.i32_fused : e.bf16_fused;
+    // Every workgroup waits for rows that other workgroups produce, so the
+    // path is only taken when the whole grid fits the device at once at this
+    // kernel's occupancy. (A cooperative launch would guarantee residency,
+    // but costs tens of microseconds on this runtime; the bounded wait with
+    // its own-rows fallback in the kernel keeps an ordinary launch correct
+    // even where the grid does not all run at once.)
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess)
+        err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err == hipSuccess)
+        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(fn),
+                                                           e.threads, 0);
+    if (err != hipSuccess)
+        return err;
+    if (tiles > (int64_t)cus * per_cu)
+        return hipErrorNotSupported;
+    // Rows per workgroup: enough to cover M with one workgroup per tile,
+    // rounded up to a power of two so that it divides BM.
+    int rpw = 1;
+    while ((int64_t)rpw * tiles < a.M)
+        rpw *= 2;
+    if (e.bm % rpw != 0)
+        return hipErrorNotSupported;
+    a.rows_per_wg = rpw;
+    // A fresh epoch per launch on this device (0 is the flags' initial value).
+    static std::atomic<unsigned> epochs[64];
+    std::atomic<unsigned> &ep = epochs[dev & 63];
+    unsigned v = ++ep;
+    if (v == 0)
+        v = ++ep;
+    a.epoch = v;
+    hipLaunchKernelGGL(fn, dim3((unsigned)tiles), dim3(e.threads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -56,8 +56,9 @@ class W8A8Linear(torch.nn.Module):
         x2 = x.reshape(-1, self.in_features)
         if x2.stride(-1) != 1:
             x2 = x2.contiguous()
-        xq, xs = ops.quant_per_token(x2)
-        out = ops.scaled_mm(xq, xs, self.w_packed, self.w_scale, self.out_features, self.bias)
+        # The per-token quant and the scaled matmul, as one library call.
+        out, _, _ = ops.quant_scaled_mm(x2, self.w_packed, self.w_scale, self.out_features,
+                                        self.bias)
         return out.reshape(*lead, self.out_features)
 
     def extra_repr(self) -> str:

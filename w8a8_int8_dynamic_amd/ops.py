@@ -16,8 +16,8 @@ from . import _lib
 from ._lib import W8A8_OUT_BF16, W8A8_OUT_I32, call
 
 __all__ = ["quant_per_token", "quant_per_channel", "prepack_weight", "unpack_weight",
-           "prepack_weight_bytes", "scaled_mm", "tile_count", "tile_name", "tile_auto",
-           "device_supported"]
+           "prepack_weight_bytes", "scaled_mm", "quant_scaled_mm", "tile_count", "tile_name",
+           "tile_auto", "device_supported"]
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -159,6 +159,53 @@ def scaled_mm(xq: torch.Tensor, xs: Optional[torch.Tensor], w_packed: torch.Tens
         call("int8_scaled_mm_tile", xq.data_ptr(), _ld(xq), ptr(xs), w_packed.data_ptr(), ptr(ws),
              ptr(bias), M, N, K, mode, out.data_ptr(), _ld(out), _stream(xq), tile)
     return out
+
+
+def quant_scaled_mm(x: torch.Tensor, w_packed: torch.Tensor, ws: Optional[torch.Tensor], N: int,
+                    bias: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+                    out: Optional[torch.Tensor] = None, tile: int = -1,
+                    xq: Optional[torch.Tensor] = None, xs: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Per-token quant of bf16 x [M, K] and the scaled matmul in one call.
+
+    Returns (out, xq, xs): out as scaled_mm returns it, and the int8 codes and
+    fp32 scales the quant produced (bit-identical to quant_per_token)."""
+    _matrix(x, "x", torch.bfloat16)
+    M, K = x.shape
+    x = _rows_aligned(x, 8)
+    if out_dtype == torch.bfloat16:
+        mode = W8A8_OUT_BF16
+        _vector(ws, N, "ws", torch.float32)
+        _vector(bias, N, "bias", torch.bfloat16)
+    elif out_dtype == torch.int32:
+        mode = W8A8_OUT_I32
+    else:
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.int32")
+    if not w_packed.is_cuda or w_packed.dtype != torch.uint8 or \
+            w_packed.numel() < prepack_weight_bytes(N, K):
+        raise ValueError("w_packed must be a uint8 device buffer from prepack_weight(N, K)")
+    if xq is None:
+        xq = _codes(M, K, x.device)
+    if xs is None:
+        xs = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _matrix(xq, "xq", torch.int8)
+    if xq.shape != (M, K):
+        raise ValueError(f"xq must have shape {(M, K)}")
+    _vector(xs, M, "xs", torch.float32)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    _matrix(out, "out", out_dtype)
+    if out.shape != (M, N):
+        raise ValueError(f"out must have shape {(M, N)}")
+
+    def ptr(t):
+        return None if t is None or mode == W8A8_OUT_I32 else t.data_ptr()
+
+    with torch.cuda.device(x.device):
+        call("int8_quant_scaled_mm_tile", x.data_ptr(), _ld(x), xq.data_ptr(), _ld(xq),
+             xs.data_ptr(), w_packed.data_ptr(), ptr(ws), ptr(bias), M, N, K, mode,
+             out.data_ptr(), _ld(out), _stream(x), tile)
+    return out, xq, xs
 
 
 def tile_count() -> int:
