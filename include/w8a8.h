@@ -173,15 +173,17 @@ w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const float *x_
  * Requirements: those of int8_scaled_mm, plus ldx >= K, x 16-byte aligned
  * and ldx a multiple of 8; x_scale is required in both output modes.
  *
- * When every workgroup of the matmul can be resident at once (true for the
- * fused-QKV layer at M 512 and smaller), one launch does both steps: each
- * workgroup quantizes a slice of rows, publishes them through per-row-tile
- * counters, and waits (bounded) only for the rows of its own tile; should a
- * wait ever run out, that workgroup quantizes its tile's rows itself, so the
- * result never depends on scheduling. The counters live in the library's
- * device memory on each GPU, so calls of this entry point must not overlap
- * on one device (issue them on one stream, or order the streams).
- * Otherwise the two steps run as two launches on `stream`.
+ * When the chosen tile is one of the main kernel's and every workgroup of
+ * the matmul can be resident at once (true for the fused-QKV layer at M 512
+ * and smaller), one launch does both steps: each workgroup quantizes a slice
+ * of rows, raises its flag (a word in the library's device memory, set to a
+ * number unique to the launch), and waits, bounded, only for the flags of
+ * its own tile's rows; should a wait ever run out, that workgroup quantizes
+ * its tile's rows itself, so the result never depends on scheduling. Calls
+ * that overlap on one device therefore stay correct (each sees only its own
+ * launch's flags) but may take that slower path. Otherwise (the small-M
+ * tiles, or a grid too large to be resident) the two steps run as two
+ * launches on `stream`.
  */
 w8a8_status_t int8_quant_scaled_mm(const uint16_t *x, int64_t ldx, int8_t *xq, int64_t ldq,
                                    float *x_scale, const void *w_packed, const float *w_scale,
@@ -195,10 +197,13 @@ w8a8_status_t int8_quant_scaled_mm_tile(const uint16_t *x, int64_t ldx, int8_t *
                                         int64_t N, int64_t K, int mode, void *out, int64_t ldo,
                                         void *stream, int tile);
 
-/* Number of tile configurations, a short name of one ("128x192/n2k2/l23":
- * tile rows x columns / wave column groups and k-groups / token and weight
- * fetch leads in stages),
- * and the tile the automatic choice picks for a shape. */
+/* Number of tile configurations, a short name of one, and the tile the
+ * automatic choice picks for a shape. Main kernel: "128x192/m1n2k2/l23" is
+ * tile rows x columns / wave row groups, column groups and k-groups / token
+ * and weight fetch leads in stages. Small-M kernel (for a few token rows; the
+ * automatic choice considers it up to 32 rows): "s16x32/k8/u4" is token rows
+ * x channels per workgroup / wavefronts splitting K / k-blocks per load
+ * group. */
 int w8a8_mm_tile_count(void);
 const char *w8a8_mm_tile_name(int tile);
 int w8a8_mm_tile_auto(int64_t M, int64_t N, int64_t K);

@@ -184,6 +184,19 @@ def test_tile_table():
         assert t == L.w8a8_mm_tile_auto(*shape)             # deterministic
 
 
+def test_tile_auto_small_m():
+    """Decode-shaped inputs (a few token rows) go to the small-M kernel, whose
+    tiles are named s<rows>x<channels>/...; from 33 rows on, and for the five
+    workloads, the main kernel's tiles are chosen."""
+    name = lambda *s: L.w8a8_mm_tile_name(L.w8a8_mm_tile_auto(*s)).decode()
+    for shape in [(1, 4096, 4096), (1, 12288, 4096), (4, 4096, 4096), (8, 3072, 12288),
+                  (32, 3072, 12288)]:
+        assert name(*shape).startswith("s"), (shape, name(*shape))
+    for shape in [(33, 3072, 12288), (64, 128, 256), (512, 4096, 4096), (512, 12288, 4096),
+                  (4096, 12288, 3072), (8192, 3072, 12288)]:
+        assert not name(*shape).startswith("s"), (shape, name(*shape))
+
+
 def test_binding_rejects_host_tensors():
     import torch
     from w8a8_int8_dynamic_amd import ops

@@ -163,7 +163,7 @@ def test_prepack_layout_and_roundtrip(ops, N, K):
 # Scaled matmul on small and mid shapes, every tile configuration
 # ---------------------------------------------------------------------------
 SHAPES = [(1, 1, 16), (37, 45, 80), (130, 200, 336), (257, 300, 1040), (64, 128, 256),
-          (300, 520, 576)]
+          (300, 520, 576), (5, 1000, 2064), (61, 777, 1104)]
 
 
 def _mm_case(seed, M, N, K, bias=True):
@@ -206,6 +206,28 @@ def test_scaled_mm_bf16_every_tile(ops, orc, M, N, K, bias):
         got = bits_np(out)
         exact = check_out(got, ref32, ref64, f"tile {ops.tile_name(t)}")
         assert exact == 1.0, f"tile {ops.tile_name(t)}: {exact:.6f} bit-exact vs fp32 epilogue"
+
+
+@pytest.mark.parametrize("M", [1, 3, 16, 32])
+def test_scaled_mm_decode_shapes_auto(ops, orc, M):
+    """A few token rows against a full-size weight (the decode case), through
+    the automatic tile choice (the small-M kernel): exact against the oracle
+    on every output, with a ragged N and K not a multiple of 64."""
+    N, K = 3000, 4112
+    inp = _mm_case(5500 + M, M, N, K, True)
+    wq, ws = orc.quant_per_channel(inp.w_f32)
+    xq, xs = orc.quant_per_token(inp.x_bf16)
+    acc = orc.gemm_i32(xq, wq)
+    ref32 = orc.epilogue_f32(acc, xs, ws, inp.bias_bf16)
+    ref64 = orc.epilogue_f64(acc, xs, ws, inp.bias_bf16)
+    assert ops.tile_name(ops.tile_auto(M, N, K)).startswith("s")
+    packed = ops.prepack_weight(torch.from_numpy(wq).to(DEV))
+    xq_d, xs_d = torch.from_numpy(xq).to(DEV), torch.from_numpy(xs).to(DEV)
+    out = ops.scaled_mm(xq_d, xs_d, packed, torch.from_numpy(ws).to(DEV), N, bf16_dev(inp.bias_bf16))
+    exact = check_out(bits_np(out), ref32, ref64, f"decode M={M}")
+    assert exact == 1.0
+    got = ops.scaled_mm(xq_d, None, packed, None, N, out_dtype=torch.int32)
+    assert np.array_equal(got.cpu().numpy(), acc)
 
 
 def test_scaled_mm_strided_output_and_unaligned_rows(ops, orc):

@@ -49,6 +49,32 @@ struct MmArgs {
     unsigned epoch;  // this launch's number on its device, never 0
 };
 
+// One tile configuration: its output tile (bm x bn), block size and
+// kernels (bf16 and int32 output; the fused quant + matmul forms, or null
+// where the configuration has none). skinny marks the small-M kernel.
+typedef void (*MmKernel)(const MmArgs);
+struct TileEntry {
+    const char *name;
+    int bm, bn, threads;
+    bool skinny;
+    MmKernel bf16, i32, bf16_fused, i32_fused;
+};
+
+// Small-M configurations (skinny_mm.hip); they follow the main kernel's in
+// the tile numbering.
+int skinny_tile_count();
+const TileEntry &skinny_tile(int i);
+
+// Physical workgroup id -> logical tile id such that each XCD (which takes
+// ids pid % 8 round-robin) receives one contiguous run of logical ids.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_remap(int pid, int tiles)
+{
+    const int q = tiles / kXcds, r = tiles % kXcds;
+    const int xcd = pid % kXcds, local = pid / kXcds;
+    return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
 int mm_tile_count();
 const char *mm_tile_name(int tile);
 int mm_tile_auto(int64_t M, int64_t N, int64_t K);

@@ -65,8 +65,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kXcds = 8;
-
 // Fused quant + matmul: workgroup w of a launch stores the launch's epoch
 // (a per-device launch number, never 0) in g_fused_flag[w] once its rows
 // are quantized. A consumer accepts a tile when every producer of its rows
@@ -80,15 +78,6 @@ __device__ unsigned g_fused_flag[kMaxFusedWgs];
 // itself, writing the same bytes as their producers, so no wave can spin
 // forever and launches that overlap on one device stay correct.
 constexpr int kSpinLimit = 1 << 12;
-
-// Physical workgroup id -> logical tile id such that each XCD (which takes
-// ids pid % 8 round-robin) receives one contiguous run of logical ids.
-__device__ __forceinline__ int xcd_remap(int pid, int tiles)
-{
-    const int q = tiles / kXcds, r = tiles % kXcds;
-    const int xcd = pid % kXcds, local = pid / kXcds;
-    return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
-}
 
 // Logical tile id -> (tm, tn): bands of kBandM M-tiles; inside a band the
 // M index runs fastest. The 32 tiles an XCD runs at once then form a block
@@ -789,18 +778,10 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
 }
 
 
-typedef void (*MmFn)(const MmArgs);
-
-struct TileEntry {
-    const char *name;
-    int bm, bn, threads;
-    MmFn bf16, i32, bf16_fused, i32_fused;
-};
-
 template <class T>
 constexpr TileEntry entry(const char *name)
 {
-    return TileEntry{name, T::BM, T::BN, T::THREADS, scaled_mm_kernel<T, false, false>,
+    return TileEntry{name, T::BM, T::BN, T::THREADS, false, scaled_mm_kernel<T, false, false>,
                      scaled_mm_kernel<T, true, false>, scaled_mm_kernel<T, false, true>,
                      scaled_mm_kernel<T, true, true>};
 }
@@ -818,34 +799,58 @@ const TileEntry kTiles[] = {
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
+const TileEntry &tile_entry(int tile)
+{
+    return tile < kNumTiles ? kTiles[tile] : skinny_tile(tile - kNumTiles);
+}
+
 }  // namespace
 
-int mm_tile_count() { return kNumTiles; }
+int mm_tile_count() { return kNumTiles + skinny_tile_count(); }
 
 const char *mm_tile_name(int tile)
 {
-    return (tile >= 0 && tile < kNumTiles) ? kTiles[tile].name : "";
+    return (tile >= 0 && tile < mm_tile_count()) ? tile_entry(tile).name : "";
 }
 
-// Automatic choice: the smallest modelled time. A tile costs the larger of
-// its MFMA time and the time to stream its operands from L2, plus a fixed
-// cost (prologue and epilogue); tiles run in full-machine rounds of one
-// workgroup per CU. Rates per CU measured on MI355X under full load: about
-// 16000 int8 MFMA ops per ns (the shader clock drops to ~2 GHz) and about 80
-// bytes per ns of L2 reads (the L2s deliver ~20 TB/s in all).
+// Automatic choice: the smallest modelled time (rates measured on MI355X
+// under full load).
+//   Main kernel: a tile costs the larger of its MFMA time and the time to
+//   stream its operands from L2, plus a fixed cost (prologue and epilogue);
+//   tiles run in full-machine rounds of one workgroup per CU. About 16000
+//   int8 MFMA ops per ns per CU (the shader clock drops to ~2 GHz) and about
+//   80 bytes per ns of L2 reads per CU (~20 TB/s in all).
+//   Small-M kernel, for up to 32 token rows (beyond that each weight byte
+//   meets enough tokens for the main kernel's tiles): the weight stream, at
+//   about 38 bytes per ns from HBM per busy CU (each row tile streams the
+//   whole weight), or the L2 reads of the workgroups if more: each k-block
+//   brings the weight fragments and one 128-byte line per token row, ~14
+//   TB/s in all; plus a fixed cost.
 int mm_tile_auto(int64_t M, int64_t N, int64_t K)
 {
-    const double cus = 256.0, mfma_ops_per_ns = 16000.0, l2_bytes_per_ns = 80.0, fixed_ns = 3000.0;
+    const double cus = 256.0;
+    const double kk = (double)round_up(K, 64), kblocks = kk / 64.0;
     int best = 0;
     double best_cost = 1e300;
-    for (int t = 0; t < kNumTiles; ++t) {
-        const TileEntry &e = kTiles[t];
-        const int64_t tiles = ceil_div(M, e.bm) * ceil_div(N, e.bn);
-        const double rounds = std::ceil((double)tiles / cus);
-        const double kk = (double)round_up(K, 64);
-        const double t_mma = 2.0 * e.bm * e.bn * kk / mfma_ops_per_ns;
-        const double t_l2 = (double)(e.bm + e.bn) * kk / l2_bytes_per_ns;
-        const double cost = rounds * (std::max(t_mma, t_l2) + fixed_ns);
+    for (int t = 0; t < mm_tile_count(); ++t) {
+        const TileEntry &e = tile_entry(t);
+        if (e.skinny && M > 32)
+            continue;
+        const int64_t tiles_m = ceil_div(M, e.bm);
+        const int64_t tiles = tiles_m * ceil_div(N, e.bn);
+        double cost;
+        if (!e.skinny) {
+            const double rounds = std::ceil((double)tiles / cus);
+            const double t_mma = 2.0 * e.bm * e.bn * kk / 16000.0;
+            const double t_l2 = (double)(e.bm + e.bn) * kk / 80.0;
+            cost = rounds * (std::max(t_mma, t_l2) + 3000.0);
+        } else {
+            const double weight = (double)tiles_m * (double)round_up(N, 16) * kk;
+            const double t_hbm = weight / (std::min((double)tiles, cus) * 38.0);
+            const double rows = (double)std::min<int64_t>(M, e.bm);
+            const double t_l2 = (double)tiles * kblocks * (e.bn / 16 * 1024.0 + rows * 128.0) / 14000.0;
+            cost = std::max(t_hbm, t_l2) + 3000.0;
+        }
         if (cost < best_cost * 0.999) {
             best_cost = cost;
             best = t;
@@ -856,7 +861,7 @@ int mm_tile_auto(int64_t M, int64_t N, int64_t K)
 
 hipError_t launch_scaled_mm(const MmArgs &a, bool out_i32, int tile, hipStream_t stream)
 {
-    const TileEntry &e = kTiles[tile];
+    const TileEntry &e = tile_entry(tile);
     const int64_t tiles = ceil_div(a.M, e.bm) * ceil_div(a.N, e.bn);
     const int threads = e.threads;
     hipLaunchKernelGGL(out_i32 ? e.i32 : e.bf16, dim3((unsigned)tiles), dim3(threads), 0, stream, a);
@@ -865,12 +870,12 @@ hipError_t launch_scaled_mm(const MmArgs &a, bool out_i32, int tile, hipStream_t
 
 hipError_t launch_quant_scaled_mm(MmArgs a, bool out_i32, int tile, hipStream_t stream)
 {
-    const TileEntry &e = kTiles[tile];
+    const TileEntry &e = tile_entry(tile);
     const int64_t tiles_m = ceil_div(a.M, e.bm);
     const int64_t tiles = tiles_m * ceil_div(a.N, e.bn);
-    if (tiles > kMaxFusedWgs)
+    MmKernel fn = out_i32 ? e.i32_fused : e.bf16_fused;
+    if (fn == nullptr || tiles > kMaxFusedWgs)
         return hipErrorNotSupported;
-    MmFn fn = out_i32 ? e.i32_fused : e.bf16_fused;
     // Every workgroup waits for rows that other workgroups produce, so the
     // path is only taken when the whole grid fits the device at once at this
     // kernel's occupancy. (A cooperative launch would guarantee residency,
