@@ -330,7 +330,7 @@ def test_workload_full_size(ops, orc, name):
 # where the grid fits the device, two launches otherwise)
 # ---------------------------------------------------------------------------
 QMM_SHAPES = [(1, 48, 64), (37, 45, 80), (130, 200, 336), (257, 300, 1040), (512, 520, 576),
-              (512, 1536, 512)]
+              (512, 1536, 512), (2, 1000, 4112), (1, 300, 16384)]
 
 
 @pytest.mark.parametrize("M,N,K", QMM_SHAPES)

@@ -1,0 +1,190 @@
+// Per-token quant inside a matmul launch: the producer and consumer sides of
+// the one-launch path of int8_quant_scaled_mm (page "Issue 5 probe: int8
+// quantized DiT serve paths on the RTX 3090 (24 GB)", "Round two"
+// kernel-path paragraph: the per-token quant that precedes the scaled
+// matmul, here run by the matmul's own workgroups).
+//
+// Protocol. Producer workgroup w quantizes rows [w*rpw, (w+1)*rpw) of x
+// (rpw = rows_per_wg) with the rule of int8_quant_per_token and then stores
+// the launch's epoch (a per-device launch number, never 0) in flag[w]. A
+// consumer accepts the rows of its tile once every producer of those rows
+// shows the current epoch, so nothing is ever reset. Flags are plain
+// coherent stores and loads, one word per producer: no read-modify-write on
+// a shared word, which would serialize at the memory side. The wait is
+// bounded; past the bound a workgroup quantizes the rows it needs itself,
+// writing the same bytes their producers write, so no wave can spin forever
+// and launches that overlap on one device stay correct.
+//
+// Coherence. Codes and scales are written with agent-scope (relaxed atomic)
+// stores, coherent across the XCDs once complete, so no write-back of the
+// producer's L2 is needed before the flag goes up. No cache of a consumer's
+// CU or XCD can hold an older copy of the rows: caches start each launch
+// clean and no workgroup reads a tile's rows before its wait.
+#pragma once
+
+#include <type_traits>
+
+#include "internal.hpp"
+#include "quant_rule.hpp"
+
+namespace w8a8 {
+namespace fused {
+
+using quant_rule::u32;
+
+// Producer flags. Every translation unit that includes this header has its
+// own array, used only by its own kernels.
+constexpr int kMaxProducers = 16384;
+static __device__ unsigned g_flag[kMaxProducers];
+
+// Bound on the polls for a tile's rows (each ~1 us; a few ms in all): far
+// beyond any real wait.
+constexpr int kSpinLimit = 1 << 12;
+
+// Rows [ra, rb) of x (bf16 [M, ldx]) into xq / xs by the THREADS threads of
+// a workgroup, with the rule of int8_quant_per_token. A row of up to
+// 8 * 8 * THREADS elements is held in registers (one read of x; two such
+// rows at a time when they fit); longer rows take an absmax pass and a codes
+// pass that re-reads the row from L2. red: 2 * THREADS / 64 words of LDS.
+// Every thread of the workgroup must call this (it holds barriers).
+template <int THREADS>
+__device__ __forceinline__ void quantize_rows(const MmArgs &a, int ra, int rb, u32 *red)
+{
+    using namespace quant_rule;
+    constexpr int NW = THREADS / 64;
+    constexpr int QCH = 8;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    // K is a multiple of 16, so every 8-code chunk is whole.
+    auto put_codes = [&](int8_t *qrow, int e, u32 lo, u32 hi) __attribute__((always_inline)) {
+        __hip_atomic_store(reinterpret_cast<uint64_t *>(qrow + e), (uint64_t)hi << 32 | lo,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto put_scale = [&](int r, float sc) __attribute__((always_inline)) {
+        if (threadIdx.x == 0)
+            __hip_atomic_store(const_cast<float *>(a.xs) + r, sc, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // One row group (1 or 2 rows) held in registers: every load of the group
+    // is issued before the reductions.
+    auto rows_in_regs = [&](auto nr_c, int r) __attribute__((always_inline)) {
+        constexpr int NR = decltype(nr_c)::value;
+        constexpr int CH = QCH / NR;
+        uint4 v[NR][CH];
+        u32 mx[NR];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const char *xrow = reinterpret_cast<const char *>(a.x + (int64_t)(r + k) * a.ldx);
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int e = (c * THREADS + (int)threadIdx.x) * 8;
+                v[k][c] = e < a.K ? load_chunk<false>(xrow, e, a.K) : make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            mx[k] = 0;
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                mx[k] = max(mx[k], chunk_absmax<false>(v[k][c]));
+            mx[k] = wave_max(mx[k]);
+            if (lane == 0)
+                red[k * NW + wave] = mx[k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < NR; ++k)
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                mx[k] = max(mx[k], red[k * NW + w]);
+        __syncthreads();                               // red is rewritten by the next group
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            float sc, inv;
+            scale_of(mx[k], false, sc, inv);
+            int8_t *qrow = const_cast<int8_t *>(a.xq) + (int64_t)(r + k) * a.ldq;
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int e = (c * THREADS + (int)threadIdx.x) * 8;
+                if (e < a.K) {
+                    u32 lo, hi;
+                    chunk_codes<false>(v[k][c], inv, lo, hi);
+                    put_codes(qrow, e, lo, hi);
+                }
+            }
+            put_scale(r + k, sc);
+        }
+    };
+    auto row_looped = [&](int r) __attribute__((always_inline)) {
+        const char *xrow = reinterpret_cast<const char *>(a.x + (int64_t)r * a.ldx);
+        int8_t *qrow = const_cast<int8_t *>(a.xq) + (int64_t)r * a.ldq;
+        u32 mx = 0;
+        for (int e = (int)threadIdx.x * 8; e < a.K; e += THREADS * 8)
+            mx = max(mx, chunk_absmax<false>(load_chunk<false>(xrow, e, a.K)));
+        mx = wave_max(mx);
+        if (lane == 0)
+            red[wave] = mx;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            mx = max(mx, red[w]);
+        __syncthreads();
+        float sc, inv;
+        scale_of(mx, false, sc, inv);
+        for (int e = (int)threadIdx.x * 8; e < a.K; e += THREADS * 8) {
+            u32 lo, hi;
+            chunk_codes<false>(load_chunk<false>(xrow, e, a.K), inv, lo, hi);
+            put_codes(qrow, e, lo, hi);
+        }
+        put_scale(r, sc);
+    };
+    int r = ra;
+    if (a.K <= (QCH / 2) * 8 * THREADS)
+        for (; r + 2 <= rb; r += 2)
+            rows_in_regs(std::integral_constant<int, 2>{}, r);
+    for (; r < rb; ++r) {
+        if (a.K <= QCH * 8 * THREADS)
+            rows_in_regs(std::integral_constant<int, 1>{}, r);
+        else
+            row_looped(r);
+    }
+}
+
+// Producer: once every thread's stores have completed, raise this
+// workgroup's flag (when it had rows to quantize). Every thread calls this.
+__device__ __forceinline__ void publish(const MmArgs &a, bool had_rows)
+{
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0 && had_rows)
+        __hip_atomic_store(&g_flag[blockIdx.x], a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Consumer: wave 0 polls the flags of producers p0 .. p0+count-1 until all
+// show this launch's epoch, or the bound runs out. Returns, in every thread,
+// true when it ran out (the caller then quantizes the rows itself).
+// decision: one word of LDS that no other phase writes meanwhile. Every
+// thread calls this.
+__device__ __forceinline__ bool wait_producers(const MmArgs &a, int p0, int count, u32 *decision)
+{
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        int it = 0;
+        for (; it < kSpinLimit; ++it) {
+            bool ready = true;
+            for (int i = lane; i < count; i += 64)
+                ready &= __hip_atomic_load(&g_flag[p0 + i], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
+            if (__all(ready))
+                break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (lane == 0)
+            decision[0] = it == kSpinLimit;
+    }
+    __syncthreads();
+    return decision[0] != 0;
+}
+
+}  // namespace fused
+}  // namespace w8a8

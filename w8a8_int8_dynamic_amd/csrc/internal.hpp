@@ -64,6 +64,10 @@ struct TileEntry {
 // the tile numbering.
 int skinny_tile_count();
 const TileEntry &skinny_tile(int i);
+// Fused quant + small-M matmul (each workgroup quantizes its own rows);
+// hipErrorNotSupported (nothing launched) when the rows are too long.
+hipError_t launch_skinny_quant_mm(const MmArgs &a, const TileEntry &e, bool out_i32,
+                                  hipStream_t stream);
 
 // Physical workgroup id -> logical tile id such that each XCD (which takes
 // ids pid % 8 round-robin) receives one contiguous run of logical ids.

@@ -51,6 +51,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "fused_rows.hpp"
 #include "internal.hpp"
 #include "quant_rule.hpp"
 
@@ -64,20 +65,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Fused quant + matmul: workgroup w of a launch stores the launch's epoch
-// (a per-device launch number, never 0) in g_fused_flag[w] once its rows
-// are quantized. A consumer accepts a tile when every producer of its rows
-// shows the current epoch, so nothing is ever reset. Flags are plain
-// coherent stores and loads, one word per producer: no read-modify-write
-// on a shared word, which would serialize at the memory side.
-constexpr int kMaxFusedWgs = 16384;
-__device__ unsigned g_fused_flag[kMaxFusedWgs];
-// Bound on the polls for a tile's rows (each ~1 us; a few ms in all): far
-// beyond any real wait. Past it a workgroup quantizes its tile's rows
-// itself, writing the same bytes as their producers, so no wave can spin
-// forever and launches that overlap on one device stay correct.
-constexpr int kSpinLimit = 1 << 12;
 
 // Logical tile id -> (tm, tn): bands of kBandM M-tiles; inside a band the
 // M index runs fastest. The 32 tiles an XCD runs at once then form a block
@@ -377,155 +364,22 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
     using Part = std::integral_constant<bool, false>;
 
     if (FUSED) {
-        // Fused quant, producer side: this workgroup quantizes rows
-        // [r0, r1) of x with the rule of int8_quant_per_token, then
-        // publishes them for its M-tile (rows_per_wg divides BM, so the rows
-        // belong to one tile). A row up to QCH * 8 * THREADS elements long is
-        // held in registers (one read); longer rows take an absmax pass and
-        // a codes pass that re-reads the row from L2.
-        using namespace quant_rule;
-        constexpr int QCH = 8;
+        // Fused quant: this workgroup quantizes rows [r0, r1) of x and
+        // publishes them (rows_per_wg divides BM, so the rows belong to one
+        // M-tile), then waits for the producers of its own tile's rows.
+        quant_rule::u32 *red = reinterpret_cast<quant_rule::u32 *>(lds);
+        // A word no other phase writes: every wave reads it after the
+        // wait's barrier while others may already be filling the ring.
+        quant_rule::u32 *decision =
+            reinterpret_cast<quant_rule::u32 *>(reinterpret_cast<char *>(lds) + T::FLAG);
         const int r0 = (int)blockIdx.x * a.rows_per_wg;
         const int r1 = min(r0 + a.rows_per_wg, a.M);
-        u32 *red = reinterpret_cast<u32 *>(lds);
-        // A word no other phase writes: every wave reads it after the
-        // barrier below while others may already be filling the ring.
-        u32 *flag = reinterpret_cast<u32 *>(reinterpret_cast<char *>(lds) + T::FLAG);
-        // Codes and scales are written with agent-scope (relaxed atomic)
-        // stores: they are coherent across the XCDs once complete, so no
-        // write-back of this XCD's L2 is needed before they are published.
-        // K is a multiple of 16, so every 8-code chunk is whole.
-        auto put_codes = [&](int8_t *qrow, int e, u32 lo, u32 hi) __attribute__((always_inline)) {
-            __hip_atomic_store(reinterpret_cast<uint64_t *>(qrow + e), (uint64_t)hi << 32 | lo,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        };
-        // One row group (1 or 2 rows) held in registers: every load of the
-        // group is issued before the reductions.
-        auto rows_in_regs = [&](auto nr_c, int r) __attribute__((always_inline)) {
-            constexpr int NR = decltype(nr_c)::value;
-            constexpr int CH = QCH / NR;
-            uint4 v[NR][CH];
-            u32 mx[NR];
-#pragma unroll
-            for (int k = 0; k < NR; ++k) {
-                const char *xrow = reinterpret_cast<const char *>(a.x + (int64_t)(r + k) * a.ldx);
-#pragma unroll
-                for (int c = 0; c < CH; ++c) {
-                    const int e = (c * T::THREADS + (int)threadIdx.x) * 8;
-                    v[k][c] = e < a.K ? load_chunk<false>(xrow, e, a.K) : make_uint4(0, 0, 0, 0);
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < NR; ++k) {
-                mx[k] = 0;
-#pragma unroll
-                for (int c = 0; c < CH; ++c)
-                    mx[k] = max(mx[k], chunk_absmax<false>(v[k][c]));
-                mx[k] = wave_max(mx[k]);
-                if (lane == 0)
-                    red[k * T::NW + wave] = mx[k];
-            }
-            __syncthreads();
-#pragma unroll
-            for (int k = 0; k < NR; ++k)
-#pragma unroll
-                for (int w = 0; w < T::NW; ++w)
-                    mx[k] = max(mx[k], red[k * T::NW + w]);
-            __syncthreads();                           // red is rewritten by the next group
-#pragma unroll
-            for (int k = 0; k < NR; ++k) {
-                float sc, inv;
-                scale_of(mx[k], false, sc, inv);
-                int8_t *qrow = const_cast<int8_t *>(a.xq) + (int64_t)(r + k) * a.ldq;
-#pragma unroll
-                for (int c = 0; c < CH; ++c) {
-                    const int e = (c * T::THREADS + (int)threadIdx.x) * 8;
-                    if (e < a.K) {
-                        u32 lo, hi;
-                        chunk_codes<false>(v[k][c], inv, lo, hi);
-                        put_codes(qrow, e, lo, hi);
-                    }
-                }
-                if (threadIdx.x == 0)
-                    __hip_atomic_store(const_cast<float *>(a.xs) + r + k, sc, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            }
-        };
-        // A row too long for registers: an absmax pass, then a codes pass
-        // that re-reads the row from L2.
-        auto row_looped = [&](int r) __attribute__((always_inline)) {
-            const char *xrow = reinterpret_cast<const char *>(a.x + (int64_t)r * a.ldx);
-            int8_t *qrow = const_cast<int8_t *>(a.xq) + (int64_t)r * a.ldq;
-            u32 mx = 0;
-            for (int e = (int)threadIdx.x * 8; e < a.K; e += T::THREADS * 8)
-                mx = max(mx, chunk_absmax<false>(load_chunk<false>(xrow, e, a.K)));
-            mx = wave_max(mx);
-            if (lane == 0)
-                red[wave] = mx;
-            __syncthreads();
-#pragma unroll
-            for (int w = 0; w < T::NW; ++w)
-                mx = max(mx, red[w]);
-            __syncthreads();
-            float sc, inv;
-            scale_of(mx, false, sc, inv);
-            for (int e = (int)threadIdx.x * 8; e < a.K; e += T::THREADS * 8) {
-                u32 lo, hi;
-                chunk_codes<false>(load_chunk<false>(xrow, e, a.K), inv, lo, hi);
-                put_codes(qrow, e, lo, hi);
-            }
-            if (threadIdx.x == 0)
-                __hip_atomic_store(const_cast<float *>(a.xs) + r, sc, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        };
-        auto quantize_rows = [&](int ra, int rb) __attribute__((always_inline)) {
-            int r = ra;
-            if (a.K <= (QCH / 2) * 8 * T::THREADS)
-                for (; r + 2 <= rb; r += 2)
-                    rows_in_regs(std::integral_constant<int, 2>{}, r);
-            for (; r < rb; ++r) {
-                if (a.K <= QCH * 8 * T::THREADS)
-                    rows_in_regs(std::integral_constant<int, 1>{}, r);
-                else
-                    row_looped(r);
-            }
-        };
-        quantize_rows(r0, r1);
-        // Every wave's stores have completed; then one thread raises this
-        // workgroup's flag.
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (threadIdx.x == 0 && r0 < r1)
-            __hip_atomic_store(&g_fused_flag[blockIdx.x], a.epoch, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-
-        // Consumer side: wait until every producer of this tile's rows has
-        // published. No cache of this CU or XCD can hold an older copy of
-        // those rows: the caches start each launch clean, and no workgroup
-        // reads a tile's rows before this wait. The wait is bounded: should
-        // it ever run out (a device that does not run every workgroup of the
-        // grid at once), this workgroup quantizes its tile's rows itself,
-        // writing the same bytes the producers write, and goes on.
+        fused::quantize_rows<T::THREADS>(a, r0, r1, red);
+        fused::publish(a, r0 < r1);
         const int rows = min(T::BM, a.M - m0);
         const int producers = (rows + a.rows_per_wg - 1) / a.rows_per_wg;
-        const int p0 = m0 / a.rows_per_wg;             // first producer of this tile
-        if (wave == 0) {
-            int it = 0;
-            for (; it < kSpinLimit; ++it) {
-                bool ready = true;
-                for (int i = lane; i < producers; i += 64)
-                    ready &= __hip_atomic_load(&g_fused_flag[p0 + i], __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
-                if (__all(ready))
-                    break;
-                __builtin_amdgcn_s_sleep(2);
-            }
-            if (lane == 0)
-                flag[0] = it == kSpinLimit;
-        }
-        __syncthreads();
-        if (flag[0]) {
-            quantize_rows(m0, m0 + rows);
+        if (fused::wait_producers(a, m0 / a.rows_per_wg, producers, decision)) {
+            fused::quantize_rows<T::THREADS>(a, m0, m0 + rows, red);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
@@ -871,34 +725,37 @@ hipError_t launch_scaled_mm(const MmArgs &a, bool out_i32, int tile, hipStream_t
 hipError_t launch_quant_scaled_mm(MmArgs a, bool out_i32, int tile, hipStream_t stream)
 {
     const TileEntry &e = tile_entry(tile);
-    const int64_t tiles_m = ceil_div(a.M, e.bm);
-    const int64_t tiles = tiles_m * ceil_div(a.N, e.bn);
+    const int64_t tiles = ceil_div(a.M, e.bm) * ceil_div(a.N, e.bn);
     MmKernel fn = out_i32 ? e.i32_fused : e.bf16_fused;
-    if (fn == nullptr || tiles > kMaxFusedWgs)
+    if (fn == nullptr)
         return hipErrorNotSupported;
+    if (e.skinny)
+        return launch_skinny_quant_mm(a, e, out_i32, stream);
+    // Rows per workgroup: enough to cover M with one workgroup per tile,
+    // rounded up to a power of two so that it divides BM.
+    int rpw = 1;
+    while ((int64_t)rpw * tiles < a.M)
+        rpw *= 2;
+    if (e.bm % rpw != 0 || ceil_div(a.M, rpw) > fused::kMaxProducers)
+        return hipErrorNotSupported;
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return err;
     // Every workgroup waits for rows that other workgroups produce, so the
     // path is only taken when the whole grid fits the device at once at this
     // kernel's occupancy. (A cooperative launch would guarantee residency,
     // but costs tens of microseconds on this runtime; the bounded wait with
-    // its own-rows fallback in the kernel keeps an ordinary launch correct
-    // even where the grid does not all run at once.)
-    int dev = 0, cus = 0, per_cu = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err == hipSuccess)
-        err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    // its own-rows fallback keeps an ordinary launch correct even where the
+    // grid does not all run at once.)
+    int cus = 0, per_cu = 0;
+    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (err == hipSuccess)
         err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(fn),
                                                            e.threads, 0);
     if (err != hipSuccess)
         return err;
     if (tiles > (int64_t)cus * per_cu)
-        return hipErrorNotSupported;
-    // Rows per workgroup: enough to cover M with one workgroup per tile,
-    // rounded up to a power of two so that it divides BM.
-    int rpw = 1;
-    while ((int64_t)rpw * tiles < a.M)
-        rpw *= 2;
-    if (e.bm % rpw != 0)
         return hipErrorNotSupported;
     a.rows_per_wg = rpw;
     // A fresh epoch per launch on this device (0 is the flags' initial value).

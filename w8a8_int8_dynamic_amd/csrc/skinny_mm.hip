@@ -24,10 +24,23 @@
 //     first MFMA, so each wave keeps U fragments in flight.
 //   - The WK partial sums meet in LDS and wave 0 applies the epilogue in the
 //     main kernel's fixed operation order.
+//   - Fused per-token quant (int8_quant_scaled_mm), for tiles of one or
+//     two rows that fit four 16-byte chunks per thread: every workgroup
+//     quantizes its own tile's rows into LDS (the rows are small and sit in
+//     L2, so repeating the work is cheap at this size) with the rule of
+//     int8_quant_per_token, and reads its token operands from there; nothing
+//     waits on another workgroup.
+//     The first load group of weights goes out before the rows are read, so
+//     the quant's latency hides behind the weight stream. The workgroup of
+//     the first channel fragment also writes the codes and scales out.
 // Ragged tails as in the main kernel: token rows past M read row M-1,
 // fragments past N read the last fragment, token chunks past K read the last
 // chunk (which meets zero weights); stores are masked.
+#include <algorithm>
+#include <type_traits>
+
 #include "internal.hpp"
+#include "quant_rule.hpp"
 
 namespace w8a8 {
 namespace {
@@ -36,6 +49,13 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Fused quant: every workgroup converts its tile's rows itself, about ten
+// VALU operations per element, which only pays below a few rows: tiles of
+// at most kQuantRows rows, and at most kQuantSlots 16-byte chunks of x per
+// thread (held in registers between the absmax and the codes).
+constexpr int kQuantRows = 2;
+constexpr int kQuantSlots = 4;
 
 // FM blocks of 16 token rows and FN fragments of 16 channels per
 // workgroup; WK wavefronts split K; U k-blocks per load group.
@@ -47,13 +67,81 @@ struct Skinny {
     static_assert(U * (FM + FN) * 4 <= 128, "operand registers");
 };
 
+// Rows m0 .. m0+rows-1 of x quantized by one workgroup of THREADS threads
+// with the rule of int8_quant_per_token: codes into tok (row r at r*pitch),
+// scales into rowscale; with `writer` also codes and scales to xq / xs. The
+// rows are read once: thread t holds chunk c of row r (elements
+// (c*THREADS + t)*8 ..+8) in slot r*cpr + c, at most kQuantSlots of them.
+// Every thread calls this (it holds barriers).
+template <int THREADS>
+__device__ __forceinline__ void quantize_tile(const MmArgs &a, int m0, int rows, int pitch,
+                                              bool writer, int8_t *tok, quant_rule::u32 *rowmax,
+                                              float *rowscale)
+{
+    using namespace quant_rule;
+    const int lane = threadIdx.x & 63;
+    const int cpr = (a.K / 8 + THREADS - 1) / THREADS;
+    const int slots = rows * cpr;
+    uint4 v[kQuantSlots];
+#pragma unroll
+    for (int s = 0; s < kQuantSlots; ++s) {
+        if (s < slots) {
+            const int r = s / cpr, e = ((s - r * cpr) * THREADS + (int)threadIdx.x) * 8;
+            // K is a multiple of 16: a chunk that starts inside the row is whole.
+            const uint16_t *xrow = a.x + (int64_t)(m0 + r) * a.ldx;
+            v[s] = e < a.K ? *reinterpret_cast<const uint4 *>(xrow + e) : make_uint4(0, 0, 0, 0);
+        }
+    }
+    if ((int)threadIdx.x < rows)
+        rowmax[threadIdx.x] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kQuantSlots; ++s) {
+        if (s < slots) {
+            const u32 m = wave_max(chunk_absmax<false>(v[s]));
+            if (lane == 0)
+                atomicMax(&rowmax[s / cpr], m);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kQuantSlots; ++s) {
+        if (s < slots) {
+            const int r = s / cpr, e = ((s - r * cpr) * THREADS + (int)threadIdx.x) * 8;
+            float sc, inv;
+            scale_of(rowmax[r], false, sc, inv);
+            if (e < a.K) {
+                u32 lo, hi;
+                chunk_codes<false>(v[s], inv, lo, hi);
+                *reinterpret_cast<v2u *>(tok + r * pitch + e) = v2u{lo, hi};
+                if (writer)
+                    *reinterpret_cast<v2u *>(const_cast<int8_t *>(a.xq) + (int64_t)(m0 + r) * a.ldq + e) =
+                        v2u{lo, hi};
+            }
+        }
+    }
+    if ((int)threadIdx.x < rows) {
+        float sc, inv;
+        scale_of(rowmax[threadIdx.x], false, sc, inv);
+        rowscale[threadIdx.x] = sc;
+        if (writer)
+            const_cast<float *>(a.xs)[m0 + threadIdx.x] = sc;
+    }
+    __syncthreads();
+}
+
 // At least 16 wavefronts per CU (128 registers each): the kernel lives on
 // the loads it keeps in flight, so occupancy counts more than ILP.
-template <class S, bool OUT_I32>
+template <class S, bool OUT_I32, bool FUSED>
 __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kernel(const MmArgs a)
 {
     // Waves 1 .. WK-1 hand their partial sums to wave 0.
     __shared__ v4i part[S::WK - 1][S::FM * S::FN][64];
+    // Fused quant: the tile's codes (rows of K + 16 bytes, sized at launch),
+    // row maxima (bit patterns of |x|) and scales.
+    extern __shared__ __attribute__((aligned(16))) int8_t tok[];
+    __shared__ quant_rule::u32 rowmax[FUSED ? S::BM : 1];
+    __shared__ float rowscale[FUSED ? S::BM : 1];
 
     const int lane = threadIdx.x & 63;
     const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -70,10 +158,15 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
     for (int j = 0; j < S::FN; ++j)
         wsrc[j] = reinterpret_cast<const v4i *>(a.wp) + (int64_t)min(nb0 + j, a.nblocks - 1) * KB * 64 +
                   lane;
+    // Token operand rows: from xq, or from the LDS codes when fused.
+    const int rows = min(S::BM, a.M - m0);
+    const int pitch = a.K + 16;
     const int8_t *tsrc[S::FM];
 #pragma unroll
-    for (int f = 0; f < S::FM; ++f)
-        tsrc[f] = a.xq + (int64_t)min(m0 + 16 * f + (lane & 15), a.M - 1) * a.ldq;
+    for (int f = 0; f < S::FM; ++f) {
+        const int r = min(16 * f + (lane & 15), rows - 1);
+        tsrc[f] = FUSED ? tok + r * pitch : a.xq + (int64_t)(m0 + r) * a.ldq;
+    }
     const int kc = 16 * (lane >> 4);
 
     v4i acc[S::FM][S::FN];
@@ -83,13 +176,19 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
         for (int j = 0; j < S::FN; ++j)
             acc[f][j] = v4i{};
 
-    auto block = [&](int kb, v4i (&w)[S::FN], v4i (&x)[S::FM]) __attribute__((always_inline)) {
+    auto wload = [&](int kb, v4i (&w)[S::FN]) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < S::FN; ++j)
             w[j] = __builtin_nontemporal_load(wsrc[j] + (int64_t)kb * 64);
+    };
+    auto tload = [&](int kb, v4i (&x)[S::FM]) __attribute__((always_inline)) {
 #pragma unroll
         for (int f = 0; f < S::FM; ++f)
             x[f] = *reinterpret_cast<const v4i *>(tsrc[f] + min(kb * 64 + kc, klast));
+    };
+    auto block = [&](int kb, v4i (&w)[S::FN], v4i (&x)[S::FM]) __attribute__((always_inline)) {
+        wload(kb, w);
+        tload(kb, x);
     };
     auto mma = [&](const v4i (&w)[S::FN], const v4i (&x)[S::FM]) __attribute__((always_inline)) {
 #pragma unroll
@@ -101,10 +200,9 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
 
     // This wave's k-blocks: wk, wk+WK, ... (mine of them). Full load groups,
     // then one partial group; within a group every load is issued before the
-    // first MFMA waits on any of them.
-    // Each workgroup starts its walk at its own offset (rot), so that the
-    // workgroups of an XCD do not all ask one L2 channel for the same token
-    // bytes at once.
+    // first MFMA waits on any of them. Each workgroup starts its walk at its
+    // own offset (rot), which spreads the workgroups of an XCD over the
+    // token bytes.
     const int mine = wk < KB ? (KB - 1 - wk) / S::WK + 1 : 0;
     const int rot = mine > 0 ? t % mine : 0;
     auto kb_of = [&](int i) __attribute__((always_inline)) {
@@ -112,6 +210,29 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
         return wk + (i >= mine ? i - mine : i) * S::WK;
     };
     int g = 0;
+    if (FUSED) {
+        // The first load group's weights go out before the token rows exist
+        // (always issued, clamped into the weight, so that no branch joins a
+        // path without them; unused when this wave has fewer k-blocks).
+        const bool pre = mine >= S::U;
+        v4i w[S::U][S::FN];
+#pragma unroll
+        for (int u = 0; u < S::U; ++u)
+            wload(min(kb_of(u), KB - 1), w[u]);
+        quantize_tile<S::THREADS>(a, m0, rows, pitch, nb0 == 0, tok, rowmax, rowscale);
+        if (pre) {
+            v4i x[S::U][S::FM];
+#pragma unroll
+            for (int u = 0; u < S::U; ++u)
+                tload(kb_of(u), x[u]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < S::U; ++u)
+                mma(w[u], x[u]);
+            __builtin_amdgcn_sched_barrier(0);
+            g = S::U;
+        }
+    }
 #pragma unroll 1
     for (; g + S::U <= mine; g += S::U) {
         v4i w[S::U][S::FN], x[S::U][S::FM];
@@ -163,7 +284,7 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
         const int m = m0 + 16 * f + (lane & 15);
         if (m >= a.M)
             continue;
-        const float xr = OUT_I32 ? 0.0f : a.xs[m];
+        const float xr = OUT_I32 ? 0.0f : FUSED ? rowscale[16 * f + (lane & 15)] : a.xs[m];
 #pragma unroll
         for (int j = 0; j < S::FN; ++j) {
             const int n = 16 * (nb0 + j) + 4 * (lane >> 4);
@@ -215,8 +336,9 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
 template <class S>
 constexpr TileEntry skinny(const char *name)
 {
-    return TileEntry{name, S::BM, S::BN, S::THREADS, true, skinny_mm_kernel<S, false>,
-                     skinny_mm_kernel<S, true>, nullptr, nullptr};
+    return TileEntry{name, S::BM, S::BN, S::THREADS, true, skinny_mm_kernel<S, false, false>,
+                     skinny_mm_kernel<S, true, false>, skinny_mm_kernel<S, false, true>,
+                     skinny_mm_kernel<S, true, true>};
 }
 
 // 16*FM token rows x 16*FN channels / WK waves along K / U k-blocks per
@@ -232,5 +354,19 @@ const TileEntry kSkinny[] = {
 
 int skinny_tile_count() { return (int)(sizeof(kSkinny) / sizeof(kSkinny[0])); }
 const TileEntry &skinny_tile(int i) { return kSkinny[i]; }
+
+hipError_t launch_skinny_quant_mm(const MmArgs &a, const TileEntry &e, bool out_i32,
+                                  hipStream_t stream)
+{
+    const int64_t rows = std::min<int64_t>(a.M, e.bm);
+    const int64_t cpr = ceil_div(a.K / 8, e.threads);
+    if (rows > kQuantRows || rows * cpr > kQuantSlots)
+        return hipErrorNotSupported;
+    const size_t lds = (size_t)(rows * (a.K + 16));
+    const int64_t tiles = ceil_div(a.M, e.bm) * ceil_div(a.N, e.bn);
+    hipLaunchKernelGGL(out_i32 ? e.i32_fused : e.bf16_fused, dim3((unsigned)tiles), dim3(e.threads),
+                       lds, stream, a);
+    return hipGetLastError();
+}
 
 }  // namespace w8a8
