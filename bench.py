@@ -5,17 +5,18 @@
 
 One step is the whole hot path on one batch: the per-token activation quant
 and the int8 MFMA matmul with its fused scale/bias/bf16 epilogue, issued as
-one library call (int8_quant_scaled_mm: a single cooperative launch when the
-matmul's grid fits the device, else the two kernels back to back). The
-weight is quantized per output channel and repacked once, before timing.
-Inputs are seeded synthetic tensors (workloads/), already resident in HBM
-when the timed region starts.
+one library call (int8_quant_scaled_mm: a single launch when the matmul's
+grid fits the device, else the two kernels back to back). The weight is
+quantized per output channel and repacked once, before timing. Inputs are
+seeded synthetic tensors (workloads/), already resident in HBM when the
+timed region starts.
 
 Printed: one JSON line with the step throughput (int8 TOP/s of 2*M*N*K per
 step), the same step as two separate calls, the roofline of the matmul
 kernel (int8_scaled_mm alone: its average launch duration from HIP events on
-the launch stream), the quant pass's GB/s, and the CPU oracle timed on a
-bounded sample of the same workload.
+the launch stream), the quant pass's GB/s, the same layer at one token
+(decode: the small-M kernel, weights streamed from HBM), and the CPU oracle
+timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -48,9 +49,13 @@ def parse_args(argv=None):
                    help="target wall time of the oracle's sampled GEMM")
     p.add_argument("--no-quant-large", action="store_true",
                    help="skip the quant bandwidth run on the FFN-down activations")
-    p.add_argument("--only", choices=["step", "step2", "mm", "quant", "copy"], default=None,
+    p.add_argument("--no-decode", action="store_true",
+                   help="skip the one-token (decode) measurement of the fused-QKV layer")
+    p.add_argument("--only", choices=["step", "step2", "mm", "quant", "copy", "decode"],
+                   default=None,
                    help="launch only this part in a loop (for profiler runs); 'copy' is a "
-                        "plain 256 MiB device copy kernel, the calibration for HBM byte counters")
+                        "plain 256 MiB device copy kernel, the calibration for HBM byte "
+                        "counters; 'decode' is the one-token fused-QKV step")
     return p.parse_args(argv)
 
 
@@ -235,6 +240,12 @@ def main(argv=None) -> int:
         quant()
         mm()
 
+    if args.only == "decode":
+        n = args.warmup + args.steps
+        decode_record(torch, ops, launches=n)
+        print(json.dumps({"only": "decode", "launches": n, "workload": "fused_qkv, M=1"}),
+              flush=True)
+        return 0
     if args.only:
         copy_src = copy_dst = None
         if args.only == "copy":
@@ -329,6 +340,8 @@ def main(argv=None) -> int:
         "source_digest": source_digest(),
     }
 
+    if not args.no_decode:
+        rec["decode"] = decode_record(torch, ops)
     if not args.no_quant_large:
         rec["quant_large"] = quant_bandwidth(torch, L, wl, stream, args.steps)
         rec["hbm_copy_reference"] = copy_reference(torch, args.steps)
@@ -338,6 +351,76 @@ def main(argv=None) -> int:
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def decode_record(torch, ops, M: int = 1, N: int = 12288, K: int = 4096, launches: int = 0) -> dict:
+    """The fused-QKV layer at one token (decode): int8_quant_scaled_mm through
+    the small-M kernel, rotating over weight copies larger than the 256 MB
+    last-level cache (each call streams its weight from HBM, as a model's
+    layers would), replayed from a HIP graph so that host launch costs stay
+    out of the timing. Every replay's output is checked against the eager
+    result. Weights and activations are seeded random data of the layer's
+    shape."""
+    g = torch.Generator(device="cpu").manual_seed(20251)
+    w = torch.randint(-127, 128, (N, K), dtype=torch.int8, generator=g).cuda()
+    x = (torch.randn((M, K), generator=g) * 2.0).to(torch.bfloat16).cuda()
+    ws = (torch.rand((N,), generator=g) * 1e-3).cuda()
+    packed = ops.prepack_weight(w)
+    copies = max(2, int(np.ceil(600e6 / packed.numel())))
+    packs = [packed] + [packed.clone() for _ in range(copies - 1)]
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    xs = torch.empty((M,), dtype=torch.float32, device="cuda")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ref = ops.quant_scaled_mm(x, packed, ws, N)[0]
+    reps = 2 * copies
+    if launches:                   # profiler runs: plain eager launches, nothing timed
+        for i in range(launches):
+            ops.quant_scaled_mm(x, packs[i % copies], ws, N, out=out, xq=xq, xs=xs)
+        torch.cuda.synchronize()
+        return {}
+
+    def capture(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(copies):
+                fn(packs[i])
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(reps):
+                fn(packs[i % copies])
+        return graph
+
+    def replay_us(graph, rounds=7):
+        ts = []
+        for _ in range(rounds):
+            out.fill_(0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            if not torch.equal(out.view(torch.int16), ref.view(torch.int16)):
+                raise RuntimeError("graph replay of the decode step differs from the eager result")
+            ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+        return float(np.median(ts))
+
+    step = replay_us(capture(lambda p: ops.quant_scaled_mm(x, p, ws, N, out=out, xq=xq, xs=xs)))
+    ops.quant_per_token(x, xq, xs)
+    mm = replay_us(capture(lambda p: ops.scaled_mm(xq, xs, p, ws, N, out=out)))
+    wbytes = packed.numel()
+    rec = {"workload": f"fused-QKV layer at {M} token(s): M={M} K={K} N={N}, bf16 out, no bias",
+           "tile": ops.tile_name(ops.tile_auto(M, N, K)),
+           "weight_copies": copies, "timing": "HIP graph replay, median per call",
+           "step_us": round(step, 3), "scaled_mm_us": round(mm, 3),
+           "weight_bytes": wbytes,
+           "step_weight_gbps": round(wbytes / (step * 1e-6) / 1e9, 1),
+           "scaled_mm_weight_gbps": round(wbytes / (mm * 1e-6) / 1e9, 1),
+           "scaled_mm_frac_hbm_peak": round(wbytes / (mm * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+    del packs, packed, w
+    torch.cuda.empty_cache()
+    return rec
 
 
 def quant_bandwidth(torch, L, wl, stream, steps: int) -> dict:

@@ -359,6 +359,46 @@ def test_quant_scaled_mm_matches_two_calls_and_oracle(ops, orc, M, N, K, bias):
         assert np.array_equal(acc.cpu().numpy(), acc_ref), ops.tile_name(t)
 
 
+@pytest.mark.parametrize("M", [1, 2, 5])
+def test_quant_scaled_mm_decode_graph_replays(ops, orc, M):
+    """The decode-shaped fused call captured in a HIP graph: several replays,
+    with eager work and synchronizations between them, each checked against
+    the oracle (M 1 and 2 take the single-launch small-M path, 5 the two
+    launches)."""
+    N, K = 1000, 4112
+    inp = wl.random_case(M, K, N, 9300 + M, bias=True)
+    x = bf16_dev(inp.x_bf16)
+    wq_ref, ws_ref = orc.quant_per_channel(inp.w_f32)
+    packed = ops.prepack_weight(torch.from_numpy(wq_ref).to(DEV))
+    ws, b = torch.from_numpy(ws_ref).to(DEV), bf16_dev(inp.bias_bf16)
+    xq_ref, xs_ref = orc.quant_per_token(inp.x_bf16)
+    acc = orc.gemm_i32(xq_ref, wq_ref)
+    ref32 = orc.epilogue_f32(acc, xs_ref, ws_ref, inp.bias_bf16)
+    ref64 = orc.epilogue_f64(acc, xs_ref, ws_ref, inp.bias_bf16)
+    xq = torch.empty((M, K), dtype=torch.int8, device=DEV)
+    xs = torch.empty((M,), dtype=torch.float32, device=DEV)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ops.quant_scaled_mm(x, packed, ws, N, b, out=out, xq=xq, xs=xs)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ops.quant_scaled_mm(x, packed, ws, N, b, out=out, xq=xq, xs=xs)
+    for i in range(4):
+        out.fill_(0)
+        xq.fill_(0)
+        xs.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(xq.cpu().numpy(), xq_ref) and np.array_equal(xs.cpu().numpy(), xs_ref)
+        exact = check_out(bits_np(out), ref32, ref64, f"replay {i}")
+        assert exact == 1.0, f"replay {i}"
+        ops.scaled_mm(xq, xs, packed, ws, N, b)    # eager work between replays
+
+
 def test_quant_scaled_mm_alternating_shapes(ops, orc):
     """Calls of different shapes back to back on one stream, each checked."""
     cases = []
