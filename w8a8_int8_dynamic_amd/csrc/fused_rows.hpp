@@ -41,16 +41,86 @@ static __device__ unsigned g_flag[kMaxProducers];
 // beyond any real wait.
 constexpr int kSpinLimit = 1 << 12;
 
+// Short rows (K <= 64 * 8 * CPL): one wavefront per row, CPL 16-byte chunks
+// per lane, 8 / CPL rows per wavefront in flight (all their loads issued
+// before the first reduction); the reduction stays inside the wavefront, so
+// there is no barrier. Wave w takes row groups w, w + NW, ... of [ra, rb).
+template <int THREADS, int CPL>
+__device__ __forceinline__ void quantize_rows_by_wave(const MmArgs &a, int ra, int rb)
+{
+    using namespace quant_rule;
+    constexpr int NW = THREADS / 64, R = 8 / CPL;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int g = ra + wave * R; g < rb; g += NW * R) {
+        uint4 v[R][CPL];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const uint16_t *xrow = a.x + (int64_t)min(g + i, rb - 1) * a.ldx;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                // K is a multiple of 16: a chunk that starts inside the row is whole.
+                const int e = (c * 64 + lane) * 8;
+                v[i][c] = e < a.K ? *reinterpret_cast<const uint4 *>(xrow + e) : make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            if (g + i >= rb)
+                break;
+            u32 mx = 0;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                mx = max(mx, chunk_absmax<false>(v[i][c]));
+            mx = wave_max(mx);
+            float sc, inv;
+            scale_of(mx, false, sc, inv);
+            int8_t *qrow = const_cast<int8_t *>(a.xq) + (int64_t)(g + i) * a.ldq;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const int e = (c * 64 + lane) * 8;
+                if (e < a.K) {
+                    u32 lo, hi;
+                    chunk_codes<false>(v[i][c], inv, lo, hi);
+                    __hip_atomic_store(reinterpret_cast<uint64_t *>(qrow + e), (uint64_t)hi << 32 | lo,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+            if (lane == 0)
+                __hip_atomic_store(const_cast<float *>(a.xs) + g + i, sc, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
 // Rows [ra, rb) of x (bf16 [M, ldx]) into xq / xs by the THREADS threads of
-// a workgroup, with the rule of int8_quant_per_token. A row of up to
-// 8 * 8 * THREADS elements is held in registers (one read of x; two such
-// rows at a time when they fit); longer rows take an absmax pass and a codes
-// pass that re-reads the row from L2. red: 2 * THREADS / 64 words of LDS.
-// Every thread of the workgroup must call this (it holds barriers).
+// a workgroup, with the rule of int8_quant_per_token. Rows of up to 4096
+// elements go one per wavefront (quantize_rows_by_wave). Longer rows use the
+// whole workgroup: a row of up to 8 * 8 * THREADS elements is held in
+// registers (one read of x; two such rows at a time when they fit); longer
+// still take an absmax pass and a codes pass that re-reads the row from L2.
+// red: 2 * THREADS / 64 words of LDS. Every thread of the workgroup must
+// call this (it may hold barriers).
 template <int THREADS>
 __device__ __forceinline__ void quantize_rows(const MmArgs &a, int ra, int rb, u32 *red)
 {
     using namespace quant_rule;
+    if (a.K <= 64 * 8) {
+        quantize_rows_by_wave<THREADS, 1>(a, ra, rb);
+        return;
+    }
+    if (a.K <= 64 * 8 * 2) {
+        quantize_rows_by_wave<THREADS, 2>(a, ra, rb);
+        return;
+    }
+    if (a.K <= 64 * 8 * 4) {
+        quantize_rows_by_wave<THREADS, 4>(a, ra, rb);
+        return;
+    }
+    if (a.K <= 64 * 8 * 8 && rb - ra > THREADS / 64) {
+        quantize_rows_by_wave<THREADS, 8>(a, ra, rb);
+        return;
+    }
     constexpr int NW = THREADS / 64;
     constexpr int QCH = 8;
     const int lane = threadIdx.x & 63;

@@ -722,6 +722,31 @@ hipError_t launch_scaled_mm(const MmArgs &a, bool out_i32, int tile, hipStream_t
     return hipGetLastError();
 }
 
+// Workgroups of a fused kernel that the device holds at once (CUs times
+// occupancy), per device, tile and output mode; 0 until first asked. The
+// runtime's occupancy query costs tens of microseconds, far more than the
+// small launches this path serves, so it runs once.
+constexpr int kCapDevices = 64, kCapTiles = 32;
+static std::atomic<int> g_capacity[kCapDevices][kCapTiles][2];
+
+static hipError_t fused_capacity(int dev, int tile, bool out_i32, MmKernel fn, int threads, int &cap)
+{
+    const bool cached = dev >= 0 && dev < kCapDevices && tile < kCapTiles;
+    if (cached && (cap = g_capacity[dev][tile][out_i32].load(std::memory_order_relaxed)) > 0)
+        return hipSuccess;
+    int cus = 0, per_cu = 0;
+    hipError_t err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err == hipSuccess)
+        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(fn),
+                                                           threads, 0);
+    if (err != hipSuccess)
+        return err;
+    cap = cus * per_cu;
+    if (cached && cap > 0)
+        g_capacity[dev][tile][out_i32].store(cap, std::memory_order_relaxed);
+    return hipSuccess;
+}
+
 hipError_t launch_quant_scaled_mm(MmArgs a, bool out_i32, int tile, hipStream_t stream)
 {
     const TileEntry &e = tile_entry(tile);
@@ -748,14 +773,11 @@ hipError_t launch_quant_scaled_mm(MmArgs a, bool out_i32, int tile, hipStream_t 
     // but costs tens of microseconds on this runtime; the bounded wait with
     // its own-rows fallback keeps an ordinary launch correct even where the
     // grid does not all run at once.)
-    int cus = 0, per_cu = 0;
-    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (err == hipSuccess)
-        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(fn),
-                                                           e.threads, 0);
+    int cap = 0;
+    err = fused_capacity(dev, tile, out_i32, fn, e.threads, cap);
     if (err != hipSuccess)
         return err;
-    if (tiles > (int64_t)cus * per_cu)
+    if (tiles > cap)
         return hipErrorNotSupported;
     a.rows_per_wg = rpw;
     // A fresh epoch per launch on this device (0 is the flags' initial value).
