@@ -118,6 +118,33 @@ size_t int8_prepack_weight_bytes(int64_t N, int64_t K);
 w8a8_status_t int8_prepack_weight(const int8_t *wq, int64_t N, int64_t K, int64_t ldw,
                                   void *w_packed, void *stream);
 
+/* Element type of a weight handed to int8_quant_prepack_weight. */
+typedef enum {
+    W8A8_W_F32 = 0,
+    W8A8_W_BF16 = 1
+} w8a8_w_dtype_t;
+
+/*
+ * int8_quant_prepack_weight - online (load-time) weight quantization: the
+ * per-output-channel rule of int8_quant_per_channel applied to a bf16 or
+ * fp32 weight w [N, ldw] (out x in), written straight into the layout of
+ * int8_prepack_weight, with the scales w_scale fp32 [N]. (Page "Online
+ * Quantization", Overview: weights and scales are computed while the model
+ * loads, from a BF16 checkpoint, with no separately prepared quantized
+ * checkpoint.)
+ *
+ * The packed bytes and scales are identical to int8_quant_per_channel of
+ * the weight (as fp32; bf16 converts exactly) followed by
+ * int8_prepack_weight; the int8 weight is never stored unpacked.
+ * w_dtype: W8A8_W_F32 or W8A8_W_BF16.
+ * Requirements: N >= 1, K >= 1, ldw >= K; w 16-byte aligned with ldw a
+ * multiple of 4 (fp32) or 8 (bf16); w_packed 16-byte aligned with
+ * int8_prepack_weight_bytes(N, K) bytes; w_scale 4-byte aligned.
+ */
+w8a8_status_t int8_quant_prepack_weight(const void *w, int w_dtype, int64_t N, int64_t K,
+                                        int64_t ldw, void *w_packed, float *w_scale,
+                                        void *stream);
+
 /*
  * int8_unpack_weight - inverse of int8_prepack_weight (debug/verification):
  * writes wq[n, k] for n < N, k < K; other bytes of wq are not touched.

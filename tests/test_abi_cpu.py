@@ -34,7 +34,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for must in ("int8_prepack_weight", "int8_quant_per_token", "int8_scaled_mm",
-                 "int8_quant_per_channel", "int8_unpack_weight", "int8_prepack_weight_bytes"):
+                 "int8_quant_per_channel", "int8_unpack_weight", "int8_prepack_weight_bytes",
+                 "int8_quant_prepack_weight"):
         assert must in names
 
 
@@ -115,6 +116,18 @@ def test_prepack_validation():
     u = L.int8_unpack_weight
     assert u(A + 8, 16, 64, A, 64, None) == ALIGN
     assert u(A, 16, 64, None, 64, None) == NULL
+
+
+def test_quant_prepack_validation():
+    def qp(w=A, dt=0, N=16, K=64, ldw=64, wp=A, ws=A):
+        return L.int8_quant_prepack_weight(w, dt, N, K, ldw, wp, ws, None)
+    assert qp(dt=2) == MODE and qp(dt=-1) == MODE
+    assert qp(N=0) == SHAPE and qp(K=0) == SHAPE and qp(ldw=63) == SHAPE
+    assert qp(w=None) == NULL and qp(wp=None) == NULL and qp(ws=None) == NULL
+    assert qp(w=A + 8) == ALIGN and qp(wp=A + 8) == ALIGN and qp(ws=A + 2) == ALIGN
+    assert qp(ldw=66) == ALIGN                              # fp32 rows: ldw % 4
+    assert qp(dt=1, ldw=68) == ALIGN                        # bf16 rows: ldw % 8
+    assert qp() == DEVICE and qp(dt=1, ldw=72) == DEVICE    # valid; no GPU here
 
 
 def mm(xq=A, ldq=64, xs=A, wp=A, ws=A, bias=None, M=4, N=16, K=64, mode=0, out=A, ldo=16, tile=-1):

@@ -159,6 +159,28 @@ def test_prepack_layout_and_roundtrip(ops, N, K):
     assert np.array_equal(ops.unpack_weight(packed, N, K).cpu().numpy(), wq)
 
 
+@pytest.mark.parametrize("N,K", [(1, 1), (17, 65), (40, 200), (33, 1000), (256, 4096),
+                                 (3072, 12288)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quant_prepack_weight(ops, orc, N, K, dtype):
+    """Online weight quant from fp32 or bf16 straight into the packed layout:
+    the packed bytes are the layout of the oracle's per-channel codes, the
+    scales are the oracle's, bit for bit (zero rows, a row below 2^-100 and a
+    row of exact ties included)."""
+    rng = np.random.default_rng(3100 + N + K)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    if N > 3:
+        w[1] = 0.0
+        w[2] = 1e-32
+        w[3] = (np.arange(K) % 5 - 2).astype(np.float32) * 0.5 * (127.0 / 254.0)
+    w_d = torch.from_numpy(w).to(DEV).to(dtype)
+    w_exact = w_d.to(torch.float32).cpu().numpy()            # bf16 widens exactly
+    wq_ref, ws_ref = orc.quant_per_channel(w_exact)
+    packed, ws = ops.quant_prepack_weight(w_d)
+    assert np.array_equal(ws.cpu().numpy(), ws_ref)
+    assert np.array_equal(packed.cpu().numpy(), packed_reference(wq_ref))
+
+
 # ---------------------------------------------------------------------------
 # Scaled matmul on small and mid shapes, every tile configuration
 # ---------------------------------------------------------------------------

@@ -30,6 +30,7 @@ SIGNATURES = {
     "int8_prepack_weight_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "int8_prepack_weight": (_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
     "int8_unpack_weight": (_int, [_vp, _i64, _i64, _vp, _i64, _vp]),
+    "int8_quant_prepack_weight": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp]),
     "int8_scaled_mm": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _i64,
                               _vp]),
     "int8_scaled_mm_tile": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp,

@@ -1,6 +1,9 @@
 """Build libw8a8.so (HIP for gfx950) in-tree with hipcc.
 
-    python -m w8a8_int8_dynamic_amd.build [--jobs N] [--save-temps]
+    python w8a8_int8_dynamic_amd/build.py [--jobs N] [--save-temps]
+
+(run as a script, or through __graft_entry__.build(): importing the package
+loads the library, which may not exist yet)
 
 Each source is compiled to an object under ``_build/`` in parallel, then
 linked into ``w8a8_int8_dynamic_amd/libw8a8.so``. Floating-point flags are

@@ -114,7 +114,7 @@ w8a8_status_t quant_common(const void *x, bool f32, int64_t M, int64_t K, int64_
 }
 
 w8a8_status_t pack_common(int64_t N, int64_t K, int64_t ldw, const void *a, const void *b,
-                          const void *packed, const char *what)
+                          const void *packed, const char *what, bool device = true)
 {
     if (N < 1 || N > kMaxRows || K < 1 || K > kMaxRows)
         return fail(W8A8_ERR_SHAPE, "%s: N and K must be in [1, 2^31)", what);
@@ -126,7 +126,7 @@ w8a8_status_t pack_common(int64_t N, int64_t K, int64_t ldw, const void *a, cons
         return fail(W8A8_ERR_NULL, "%s: NULL tensor pointer", what);
     if (!aligned(packed, 16))
         return fail(W8A8_ERR_ALIGN, "%s: packed weight must be 16-byte aligned", what);
-    return check_device();
+    return device ? check_device() : ok();
 }
 
 }  // namespace
@@ -165,6 +165,30 @@ W8A8_API w8a8_status_t int8_prepack_weight(const int8_t *wq, int64_t N, int64_t 
     return launched(w8a8::launch_prepack(wq, N, K, ldw, w_packed,
                                          reinterpret_cast<hipStream_t>(stream)),
                     "int8_prepack_weight");
+}
+
+W8A8_API w8a8_status_t int8_quant_prepack_weight(const void *w, int w_dtype, int64_t N, int64_t K,
+                                                 int64_t ldw, void *w_packed, float *w_scale,
+                                                 void *stream)
+{
+    const char *what = "int8_quant_prepack_weight";
+    if (w_dtype != W8A8_W_F32 && w_dtype != W8A8_W_BF16)
+        return fail(W8A8_ERR_MODE, "%s: unknown weight dtype %d", what, w_dtype);
+    const bool f32 = w_dtype == W8A8_W_F32;
+    w8a8_status_t st = pack_common(N, K, ldw, w, w_packed, w_packed, what, false);
+    if (st != W8A8_OK)
+        return st;
+    if (!w_scale)
+        return fail(W8A8_ERR_NULL, "%s: NULL tensor pointer", what);
+    if (!aligned(w, 16) || ldw % (f32 ? 4 : 8) != 0 || !aligned(w_scale, 4))
+        return fail(W8A8_ERR_ALIGN, "%s: w must be 16-byte aligned with ldw a multiple of %d, "
+                    "w_scale 4-byte aligned", what, f32 ? 4 : 8);
+    st = check_device();
+    if (st != W8A8_OK)
+        return st;
+    return launched(w8a8::launch_quant_prepack(w, f32, N, K, ldw, w_packed, w_scale,
+                                               reinterpret_cast<hipStream_t>(stream)),
+                    what);
 }
 
 W8A8_API w8a8_status_t int8_unpack_weight(const void *w_packed, int64_t N, int64_t K, int8_t *wq,

@@ -25,6 +25,10 @@ hipError_t launch_prepack(const int8_t *wq, int64_t N, int64_t K, int64_t ldw, v
                           hipStream_t stream);
 hipError_t launch_unpack(const void *packed, int64_t N, int64_t K, int8_t *wq, int64_t ldw,
                          hipStream_t stream);
+// Per-channel quant of a bf16 (w_f32 false) or fp32 weight [N, ldw] straight
+// into the packed layout, with the fp32 scales.
+hipError_t launch_quant_prepack(const void *w, bool w_f32, int64_t N, int64_t K, int64_t ldw,
+                                void *packed, float *w_scale, hipStream_t stream);
 
 // ---- scaled matmul (scaled_mm.hip) ----
 struct MmArgs {

@@ -20,9 +20,9 @@ __all__ = ["W8A8Linear"]
 class W8A8Linear(torch.nn.Module):
     """y = bf16( int8(x) @ int8(W)^T * x_scale * w_scale (+ bias) ).
 
-    Build with ``from_float`` (per-channel weight quantization on the GPU,
-    then the load-time repack) or ``from_quantized`` (int8 weights and fp32
-    scales already made offline).
+    Build with ``from_float`` (online per-channel weight quantization on the
+    GPU, written straight into the load-time layout) or ``from_quantized``
+    (int8 weights and fp32 scales already made offline).
     """
 
     def __init__(self, w_packed: torch.Tensor, w_scale: torch.Tensor, out_features: int,
@@ -46,8 +46,15 @@ class W8A8Linear(torch.nn.Module):
 
     @classmethod
     def from_float(cls, weight: torch.Tensor, bias: Optional[torch.Tensor] = None) -> "W8A8Linear":
-        wq, ws = ops.quant_per_channel(weight.to(torch.float32).contiguous())
-        return cls.from_quantized(wq, ws, bias)
+        """bf16 and fp32 weights are quantized as they are; other float types
+        (fp16) are widened to fp32 first, which is exact."""
+        w = weight if weight.dtype in (torch.bfloat16, torch.float32) else weight.to(torch.float32)
+        N, K = w.shape
+        packed, ws = ops.quant_prepack_weight(w.contiguous())
+        if not torch.isfinite(ws).all():
+            raise ValueError("weight scales must be finite")
+        b = None if bias is None else bias.to(torch.bfloat16).contiguous()
+        return cls(packed, ws, N, K, b)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         if x.shape[-1] != self.in_features:

@@ -15,7 +15,7 @@ import torch
 from . import _lib
 from ._lib import W8A8_OUT_BF16, W8A8_OUT_I32, call
 
-__all__ = ["quant_per_token", "quant_per_channel", "prepack_weight", "unpack_weight",
+__all__ = ["quant_per_token", "quant_per_channel", "prepack_weight", "quant_prepack_weight", "unpack_weight",
            "prepack_weight_bytes", "scaled_mm", "quant_scaled_mm", "tile_count", "tile_name",
            "tile_auto", "device_supported"]
 
@@ -115,6 +115,24 @@ def prepack_weight(wq: torch.Tensor) -> torch.Tensor:
     with torch.cuda.device(wq.device):
         call("int8_prepack_weight", wq.data_ptr(), N, K, _ld(wq), packed.data_ptr(), _stream(wq))
     return packed
+
+
+def quant_prepack_weight(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Online per-output-channel quantization of a bf16 or fp32 weight [N, K],
+    written straight into the prepacked layout: (packed uint8 bytes, fp32 [N]).
+    The same bytes and scales as prepack_weight(quant_per_channel(w))."""
+    if w.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"w must be bfloat16 or float32, got {w.dtype}")
+    _matrix(w, "w", w.dtype)
+    N, K = w.shape
+    f32 = w.dtype == torch.float32
+    w = _rows_aligned(w, 4 if f32 else 8)
+    packed = torch.empty((prepack_weight_bytes(N, K),), dtype=torch.uint8, device=w.device)
+    ws = torch.empty((N,), dtype=torch.float32, device=w.device)
+    with torch.cuda.device(w.device):
+        call("int8_quant_prepack_weight", w.data_ptr(), 0 if f32 else 1, N, K, _ld(w),
+             packed.data_ptr(), ws.data_ptr(), _stream(w))
+    return packed, ws
 
 
 def unpack_weight(packed: torch.Tensor, N: int, K: int) -> torch.Tensor:
