@@ -9,8 +9,8 @@ this module compiles it with gcc on first use and wraps it for NumPy arrays.
 What each function computes, and the passage of the pages it follows, is
 stated in ``oracle.c``.
 
-Every array crossing this boundary is C-contiguous; bf16 values are carried
-as ``uint16`` bit patterns.
+Every array crossing this boundary is C-contiguous; bf16 and fp16 values are
+carried as ``uint16`` bit patterns.
 """
 from __future__ import annotations
 
@@ -55,6 +55,9 @@ class Oracle:
             "oracle_gemm_i32_rows": [vp, i64, vp, i64, vp, i64, i64, i64, vp, i64],
             "oracle_epilogue_f32": [vp, i64, i64, i64, vp, vp, vp, vp, i64],
             "oracle_epilogue_f64": [vp, i64, i64, i64, vp, vp, vp, vp, i64],
+            "oracle_quant_rows_f16": [vp, i64, i64, i64, vp, i64, vp],
+            "oracle_epilogue_f32_f16": [vp, i64, i64, i64, vp, vp, vp, vp, i64],
+            "oracle_epilogue_f64_f16": [vp, i64, i64, i64, vp, vp, vp, vp, i64],
         }.items():
             fn = getattr(lib, name)
             fn.argtypes = args
@@ -63,6 +66,10 @@ class Oracle:
         lib.oracle_float_to_bf16.restype = ctypes.c_uint16
         lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
         lib.oracle_double_to_bf16.restype = ctypes.c_uint16
+        lib.oracle_double_to_f16.argtypes = [ctypes.c_double]
+        lib.oracle_double_to_f16.restype = ctypes.c_uint16
+        lib.oracle_f16_to_float.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_to_float.restype = ctypes.c_float
         self.lib = lib
 
     @staticmethod
@@ -80,6 +87,16 @@ class Oracle:
         s = np.empty(M, dtype=np.float32)
         self._check(self.lib.oracle_quant_rows_bf16(_p(x), M, K, K, _p(q), K, _p(s)),
                     "quant_per_token")
+        return q, s
+
+    def quant_per_token_f16(self, x_f16: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+        """Step 1 on fp16 activations (uint16 bit patterns)."""
+        x = np.ascontiguousarray(x_f16, dtype=np.uint16)
+        M, K = x.shape
+        q = np.empty((M, K), dtype=np.int8)
+        s = np.empty(M, dtype=np.float32)
+        self._check(self.lib.oracle_quant_rows_f16(_p(x), M, K, K, _p(q), K, _p(s)),
+                    "quant_per_token_f16")
         return q, s
 
     # -- step 2: per-output-channel weight quantization --------------------
@@ -132,6 +149,20 @@ class Oracle:
     def epilogue_f64(self, acc, xs, ws, bias=None) -> np.ndarray:
         """bf16 bits of acc*xs*ws (+bias) evaluated in fp64, rounded once."""
         return self._epilogue(self.lib.oracle_epilogue_f64, acc, xs, ws, bias)
+
+    def epilogue_f32_f16(self, acc, xs, ws, bias=None) -> np.ndarray:
+        """fp16 bits of fl(fl(fl(acc)*xs)*ws) (+fp16 bias), fixed fp32 order."""
+        return self._epilogue(self.lib.oracle_epilogue_f32_f16, acc, xs, ws, bias)
+
+    def epilogue_f64_f16(self, acc, xs, ws, bias=None) -> np.ndarray:
+        """fp16 bits of acc*xs*ws (+fp16 bias) evaluated in fp64, rounded once."""
+        return self._epilogue(self.lib.oracle_epilogue_f64_f16, acc, xs, ws, bias)
+
+    def double_to_f16(self, d: float) -> int:
+        return int(self.lib.oracle_double_to_f16(d))
+
+    def f16_to_float(self, h: int) -> float:
+        return float(self.lib.oracle_f16_to_float(h))
 
     def float_to_bf16(self, f: float) -> int:
         return int(self.lib.oracle_float_to_bf16(f))

@@ -32,7 +32,12 @@
  *   - epilogue in fp32, each step rounded once, no fused multiply-add:
  *     t = fl(fl(fl(acc) * xs) * ws); t = fl(t + bias); out = bf16_rne(t);
  *   - a second epilogue evaluates the same value in fp64 and rounds once
- *     to bf16, for tolerance checks independent of the fp32 order.
+ *     to bf16, for tolerance checks independent of the fp32 order;
+ *   - the fp16 twin (the pages run the layer with bf16 and with fp16
+ *     activations: "Issue 5 probe ...", the Marlin isolation paragraph)
+ *     widens fp16 activations exactly, takes its bias in fp16 and rounds
+ *     the same fp32 value (or the fp64 one) to fp16, nearest-even, with
+ *     gradual underflow and overflow to infinity.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC.
  * fp32 arithmetic here is IEEE single precision (SSE), round-to-nearest-even.
@@ -87,6 +92,51 @@ static uint16_t double_to_bf16_rne(double d)
     return (uint16_t)u;
 }
 
+/* IEEE binary16 bits -> float (exact: every half is a float). */
+static float f16_bits_to_float(uint16_t h)
+{
+    int sign = h >> 15, e = (h >> 10) & 0x1f, m = h & 0x3ff;
+    float v;
+    if (e == 0)
+        v = ldexpf((float)m, -24);                  /* zero and subnormals: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexpf((float)(m | 0x400), e - 25);     /* (1024 + m) * 2^(e-25) */
+    return sign ? -v : v;
+}
+
+/* Round a double to binary16 once, nearest-even, with gradual underflow
+ * (step 2^-24 below 2^-14) and overflow to infinity: a magnitude rounds to
+ * infinity when it is at least 65520 (half way between 65504, the largest
+ * half, and 65536, the next step). NaN maps to a quiet NaN. A float input
+ * is widened to double exactly, so the same routine rounds floats once. */
+static uint16_t double_to_f16_rne(double d)
+{
+    if (isnan(d))
+        return 0x7e00u;
+    uint16_t sign = signbit(d) ? 0x8000u : 0x0000u;
+    double a = fabs(d);
+    if (a >= 65520.0)
+        return sign | 0x7c00u;
+    int e;
+    frexp(a, &e);                                   /* a = m * 2^e, m in [0.5, 1) */
+    int q = e - 11;                                 /* step of an 11-bit significand */
+    if (q < -24)
+        q = -24;                                    /* subnormal step 2^-24 */
+    double r = nearbyint(ldexp(a, -q));             /* a / 2^q, ties to even */
+    /* r * 2^q is the rounded magnitude; r may have carried into 2^11. */
+    if (r == 0.0)
+        return sign;
+    int k;
+    frexp(r, &k);                                   /* r < 2^k */
+    int exp_unbiased = q + k - 1;                   /* value in [2^exp, 2^(exp+1)) */
+    if (exp_unbiased < -14)                         /* subnormal: bits are r itself */
+        return sign | (uint16_t)r;
+    uint32_t sig = (uint32_t)ldexp(r, 11 - k);      /* 11 bits, leading one at bit 10 */
+    return sign | (uint16_t)((exp_unbiased + 15) << 10) | (uint16_t)(sig & 0x3ffu);
+}
+
 /* One row of floats -> int8 codes + fp32 scale (steps 1 and 2 above). */
 static void quantize_row(const float *v, int64_t K, int8_t *q, float *scale)
 {
@@ -136,6 +186,34 @@ int oracle_quant_rows_bf16(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                 const uint16_t *xr = x + m * ldx;
                 for (int64_t k = 0; k < K; ++k)
                     row[k] = bf16_bits_to_float(xr[k]);
+                quantize_row(row, K, q + m * ldq, &scale[m]);
+            }
+            free(row);
+        }
+    }
+    return failed ? ORACLE_ERR_ARGS : ORACLE_OK;
+}
+
+/* Per-token quantization of fp16 activations X[M, ldx] (first K columns):
+ * the same as oracle_quant_rows_bf16 with fp16 widening. */
+int oracle_quant_rows_f16(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                          int8_t *q, int64_t ldq, float *scale)
+{
+    if (M < 0 || K < 1 || ldx < K || ldq < K || (M > 0 && (!x || !q || !scale)))
+        return ORACLE_ERR_ARGS;
+    int failed = 0;
+#pragma omp parallel reduction(| : failed)
+    {
+        float *row = (float *)malloc((size_t)K * sizeof(float));
+        if (!row) {
+            failed = 1;
+        } else {
+            int64_t m;
+#pragma omp for schedule(static)
+            for (m = 0; m < M; ++m) {
+                const uint16_t *xr = x + m * ldx;
+                for (int64_t k = 0; k < K; ++k)
+                    row[k] = f16_bits_to_float(xr[k]);
                 quantize_row(row, K, q + m * ldq, &scale[m]);
             }
             free(row);
@@ -227,6 +305,51 @@ int oracle_epilogue_f64(const int32_t *acc, int64_t ldc, int64_t M, int64_t N,
     return ORACLE_OK;
 }
 
+/* The fp16 twin of the epilogue: bias and output are fp16 bits; the fp32
+ * steps are the same, the last rounding goes to fp16 (nearest-even). */
+int oracle_epilogue_f32_f16(const int32_t *acc, int64_t ldc, int64_t M, int64_t N,
+                            const float *xs, const float *ws, const uint16_t *bias,
+                            uint16_t *out, int64_t ldo)
+{
+    if (M < 0 || N < 1 || ldc < N || ldo < N || (M > 0 && (!acc || !xs || !ws || !out)))
+        return ORACLE_ERR_ARGS;
+    int64_t m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            float t = (float)acc[m * ldc + n];
+            t = t * xs[m];
+            t = t * ws[n];
+            if (bias)
+                t = t + f16_bits_to_float(bias[n]);
+            out[m * ldo + n] = double_to_f16_rne((double)t);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* The same value in fp64, rounded once to fp16. */
+int oracle_epilogue_f64_f16(const int32_t *acc, int64_t ldc, int64_t M, int64_t N,
+                            const float *xs, const float *ws, const uint16_t *bias,
+                            uint16_t *out, int64_t ldo)
+{
+    if (M < 0 || N < 1 || ldc < N || ldo < N || (M > 0 && (!acc || !xs || !ws || !out)))
+        return ORACLE_ERR_ARGS;
+    int64_t m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double t = (double)acc[m * ldc + n] * (double)xs[m] * (double)ws[n];
+            if (bias)
+                t += (double)f16_bits_to_float(bias[n]);
+            out[m * ldo + n] = double_to_f16_rne(t);
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* Exposed for the pins: the scalar conversions used above. */
 uint16_t oracle_float_to_bf16(float f) { return float_to_bf16_rne(f); }
 uint16_t oracle_double_to_bf16(double d) { return double_to_bf16_rne(d); }
+uint16_t oracle_double_to_f16(double d) { return double_to_f16_rne(d); }
+float oracle_f16_to_float(uint16_t h) { return f16_bits_to_float(h); }

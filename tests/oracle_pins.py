@@ -9,7 +9,7 @@ oracle disagrees with what the pages or the mathematics fix:
   idempotence, stacking of fused QKV blocks);
 * brute force with Python integers and exact rationals on tiny inputs;
 * library routines on special cases (NumPy int64/float64 matmul, NumPy
-  float32 division, torch's bf16 cast);
+  float32 division, torch's bf16 cast, NumPy's half-precision conversions);
 * the statistics the pages print (0.17 % rel-L2 at three shapes; the
   missing-act_scale signature: 97 % error and norm ratio E[act_scale]).
 
@@ -263,6 +263,111 @@ def pin_epilogue_exact(o):
 
 
 # ---------------------------------------------------------------------------
+# The fp16 twin: conversions, quant on fp16 rows, fp16 epilogue
+# ---------------------------------------------------------------------------
+def _exact_f16(v: Fraction) -> int:
+    """IEEE binary16 bits of the exact rational v, nearest-even, with gradual
+    underflow (step 2^-24 below 2^-14) and overflow to infinity."""
+    neg = v < 0
+    v = -v if neg else v
+    sign = 0x8000 if neg else 0
+    if v == 0:
+        return sign
+    e = v.numerator.bit_length() - v.denominator.bit_length()
+    if Fraction(2) ** e > v:
+        e -= 1
+    ulp = Fraction(2) ** (max(e, -14) - 10)        # 11 significant bits, or subnormal step
+    t = v / ulp
+    r = int(t)
+    frac = t - r
+    if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and r % 2 == 1):
+        r += 1
+    val = r * ulp
+    if val > 65504:
+        return sign | 0x7C00
+    h = np.float16(float(val))
+    assert Fraction(float(h)) == val
+    return sign | int(np.asarray(h).view(np.uint16))
+
+
+def pin_f16_conversions(o):
+    # every binary16 pattern widens like NumPy's half type
+    for h in range(0x10000):
+        ref = float(np.array([h], np.uint16).view(np.float16)[0])
+        got = o.f16_to_float(h)
+        assert got == ref or (np.isnan(got) and np.isnan(ref)), hex(h)
+    # hand-built ties and edges
+    for d, bits in [(1.0 + 2.0 ** -11, 0x3C00), (1.0 + 3 * 2.0 ** -11, 0x3C02),
+                    (1.0 + 2.0 ** -11 + 2.0 ** -40, 0x3C01), (2.0 ** -25, 0x0000),
+                    (3 * 2.0 ** -25, 0x0002), (2.0 ** -25 + 2.0 ** -60, 0x0001),
+                    (2.0 ** -14 - 2.0 ** -25, 0x0400), (65504.0, 0x7BFF), (65519.99, 0x7BFF),
+                    (65520.0, 0x7C00), (-65520.0, 0xFC00), (-0.0, 0x8000), (1e30, 0x7C00)]:
+        assert o.double_to_f16(d) == bits, (d, hex(o.double_to_f16(d)))
+    # random doubles over the whole range: exact rational rounding and
+    # NumPy's own double -> half conversion
+    rng = np.random.default_rng(21)
+    d = rng.standard_normal(3000) * 10.0 ** rng.uniform(-9, 5.5, 3000)
+    ref = d.astype(np.float16).view(np.uint16)
+    for v, r in zip(d, ref):
+        got = o.double_to_f16(float(v))
+        assert got == int(r) == _exact_f16(Fraction(float(v))), v
+
+
+def pin_quant_f16(o):
+    # values exact in both bf16 and fp16 (8 significant bits, fp16's normal
+    # range): the fp16 quant must equal the bf16 one, codes and scales
+    rng = np.random.default_rng(22)
+    v = (rng.integers(-255, 256, (24, 96)) * 2.0 ** rng.integers(-12, 6, (24, 1))).astype(np.float32)
+    v[3] = 0.0
+    v[5, 7] = -255.0 * 2.0 ** -12                      # argmax negative
+    h = v.astype(np.float16).view(np.uint16)
+    q16, s16 = o.quant_per_token_f16(h)
+    qb, sb = o.quant_per_token(_bits(v))
+    assert np.array_equal(q16, qb) and np.array_equal(s16, sb)
+    assert s16[3] == 0 and not q16[3].any()
+    # random fp16 rows incl. subnormals: |x - q*s| <= s/2 (+fp32 slack), argmax -> +-127
+    x = (rng.standard_normal((32, 200)) * 10.0 ** rng.uniform(-6, 4, (32, 1))).astype(np.float16)
+    x[0, :] = np.float16(6e-8)                         # subnormal-only row
+    q, s = o.quant_per_token_f16(x.view(np.uint16))
+    xf = x.astype(np.float64)
+    err = np.abs(xf - q.astype(np.float64) * s.astype(np.float64)[:, None])
+    assert np.all(err <= s.astype(np.float64)[:, None] * (0.5 + 1e-5))
+    am = np.argmax(np.abs(xf), axis=1)
+    assert np.all(np.abs(q[np.arange(32), am]) == 127)
+
+
+def pin_epilogue_f16_exact(o):
+    rng = np.random.default_rng(23)
+    M, N = 6, 7
+    acc = rng.integers(-2 ** 20, 2 ** 20, (M, N)).astype(np.int32)
+    acc[0, 0] = 2 ** 31 - 1                            # overflows fp16 -> inf
+    acc[1, 1] = -2 ** 31
+    acc[2, 2] = 3                                      # lands in the subnormal range
+    xs = (rng.uniform(0.01, 1, M)).astype(np.float32)
+    ws = (rng.uniform(1e-4, 1e-2, N)).astype(np.float32)
+    xs[0] = xs[1] = 1.0
+    ws[0] = ws[1] = 1.0
+    xs[2], ws[2] = np.float32(2.0 ** -12), np.float32(2.0 ** -12)
+    bias = (rng.standard_normal(N) * 0.01).astype(np.float16).view(np.uint16)
+    bias[2] = 0
+    for b in (None, bias):
+        got = o.epilogue_f64_f16(acc, xs, ws, b)
+        for m in range(M):
+            for n in range(N):
+                v = Fraction(int(acc[m, n])) * Fraction(float(xs[m])) * Fraction(float(ws[n]))
+                if b is not None:
+                    v += Fraction(float(np.array([b[n]], np.uint16).view(np.float16)[0]))
+                assert got[m, n] == _exact_f16(v), (m, n)
+    assert got[0, 0] == 0x7C00 and got[1, 1] == 0xFC00
+    # the fixed-order fp32 epilogue rounds the fp32 value once to fp16: it
+    # stays within one fp16 step of the exact value (same sign, so the bit
+    # patterns differ by at most one)
+    f32 = o.epilogue_f32_f16(acc, xs, ws, bias).astype(np.int32)
+    f64 = o.epilogue_f64_f16(acc, xs, ws, bias).astype(np.int32)
+    assert np.all(np.abs(f32 - f64) <= 1)
+
+
+# ---------------------------------------------------------------------------
 # Whole layer
 # ---------------------------------------------------------------------------
 def _dequant_reference(xq, xs, wq, ws, bias=None):
@@ -379,7 +484,7 @@ def pin_pages_missing_act_scale(o, rows: int = 64):
 
 
 FAST_PINS = [pin_quant_ties, pin_quant_zero_rows, pin_quant_invariants, pin_gemm_bruteforce,
-             pin_gemm_numpy, pin_bf16_rounding, pin_epilogue_exact, pin_layer_vs_numpy,
-             pin_fused_qkv_stack]
+             pin_gemm_numpy, pin_bf16_rounding, pin_epilogue_exact, pin_f16_conversions,
+             pin_quant_f16, pin_epilogue_f16_exact, pin_layer_vs_numpy, pin_fused_qkv_stack]
 PAGE_PINS = [pin_pages_rel_l2, pin_pages_missing_act_scale]
 ALL_PINS = FAST_PINS + PAGE_PINS

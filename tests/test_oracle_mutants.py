@@ -31,6 +31,14 @@ MUTANTS = {
     "bf16_round_half_up": ("u += 0x7fffu + lsb;", "u += 0x8000u + 0u * lsb;"),
     "xs_indexed_by_column": ("t = t * xs[m];", "t = t * xs[n % M];"),
     "f64_double_rounding": ("double r = nearbyint(ldexp(m, 8));", "double r = nearbyint(ldexp((float)m, 8));"),
+    "f16_truncate": ("double r = nearbyint(ldexp(a, -q));", "double r = floor(ldexp(a, -q));"),
+    "f16_coarse_subnormals": ("q = -24;                                    /* subnormal step 2^-24 */",
+                              "q = -23;"),
+    "f16_overflow_early": ("if (a >= 65520.0)", "if (a > 65504.0)"),
+    "f16_decode_exponent": ("v = ldexpf((float)(m | 0x400), e - 25);", "v = ldexpf((float)(m | 0x400), e - 24);"),
+    "f16_bias_dropped": ("t = t + f16_bits_to_float(bias[n]);", "t = t;"),
+    "f16_out_through_bf16": ("out[m * ldo + n] = double_to_f16_rne((double)t);",
+                             "out[m * ldo + n] = double_to_f16_rne((double)bf16_bits_to_float(float_to_bf16_rne(t)));"),
 }
 
 
