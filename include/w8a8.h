@@ -48,11 +48,13 @@ typedef enum w8a8_status {
     W8A8_ERR_HIP = 6     /* the HIP runtime reported an error when launching */
 } w8a8_status_t;
 
-/* Output of int8_scaled_mm: the bf16 layer output, or the raw int32
- * accumulators (debug mode; the scales and bias are then ignored). */
+/* Output of int8_scaled_mm: the layer output in bf16 or fp16, or the raw
+ * int32 accumulators (debug mode; the scales and bias are then ignored).
+ * The bias, when given, has the output's type (bf16 or fp16 bits). */
 typedef enum w8a8_mm_out {
     W8A8_OUT_BF16 = 0,
-    W8A8_OUT_I32 = 1
+    W8A8_OUT_I32 = 1,
+    W8A8_OUT_F16 = 2
 } w8a8_mm_out_t;
 
 /* Largest K accepted by int8_scaled_mm: the largest multiple of 16 with
@@ -79,6 +81,16 @@ typedef enum w8a8_mm_out {
  */
 w8a8_status_t int8_quant_per_token(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                                    int8_t *xq, int64_t ldq, float *x_scale, void *stream);
+
+/*
+ * int8_quant_per_token_f16 - int8_quant_per_token for fp16 activations (the
+ * pages run the layer with bf16 and with fp16 activations: page "Issue 5
+ * probe ...", the isolation table's two activation columns). Each element
+ * is widened to fp32 exactly; the rule, outputs and requirements are those
+ * of int8_quant_per_token (x holds fp16 bit patterns).
+ */
+w8a8_status_t int8_quant_per_token_f16(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                                       int8_t *xq, int64_t ldq, float *x_scale, void *stream);
 
 /*
  * int8_quant_per_channel - per-output-channel symmetric weight quantization.
@@ -162,10 +174,13 @@ w8a8_status_t int8_unpack_weight(const void *w_packed, int64_t N, int64_t K, int
  *   acc[m,n] = sum_{k<K} xq[m,k] * wq[n,k]                (exact, int32)
  *   W8A8_OUT_BF16: out[m,n] = bf16_rne( fl32(fl32(fl32(acc) * x_scale[m]) * w_scale[n])
  *                                        [+ bias[n], rounded to fp32] )
+ *   W8A8_OUT_F16:  the same fp32 value (with an fp16 bias) rounded to fp16,
+ *                  nearest-even (overflow gives infinity)
  *   W8A8_OUT_I32:  out[m,n] = acc[m,n]
  * Inputs: xq int8 [M, ldq]; x_scale fp32 [M]; w_packed from
- * int8_prepack_weight(N, K); w_scale fp32 [N]; bias bf16 [N] or NULL.
- * Output: bf16 or int32 [M, ldo].
+ * int8_prepack_weight(N, K); w_scale fp32 [N]; bias [N] in the output's
+ * type (bf16 or fp16 bits) or NULL.
+ * Output: bf16, fp16 or int32 [M, ldo].
  * Requirements: M >= 0 (M == 0 is a no-op), N >= 1, 16 <= K <= W8A8_MAX_K
  * with K a multiple of 16, ldq >= K, ldo >= N; xq and w_packed 16-byte
  * aligned, ldq a multiple of 16; out aligned to its element size. In I32
@@ -196,7 +211,9 @@ w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const float *x_
  *
  * Inputs: x bf16 [M, ldx]; w_packed, w_scale, bias as for int8_scaled_mm.
  * Outputs: the codes xq int8 [M, ldq] and scales x_scale fp32 [M] (written,
- * as int8_quant_per_token writes them) and out (bf16 or int32 [M, ldo]).
+ * as int8_quant_per_token writes them) and out ([M, ldo] in the mode's type).
+ * The single-launch paths below serve modes W8A8_OUT_BF16 and W8A8_OUT_I32;
+ * W8A8_OUT_F16 from bf16 activations runs as two launches.
  * Requirements: those of int8_scaled_mm, plus ldx >= K, x 16-byte aligned
  * and ldx a multiple of 8; x_scale is required in both output modes.
  *
@@ -216,6 +233,26 @@ w8a8_status_t int8_quant_scaled_mm(const uint16_t *x, int64_t ldx, int8_t *xq, i
                                    float *x_scale, const void *w_packed, const float *w_scale,
                                    const uint16_t *bias, int64_t M, int64_t N, int64_t K, int mode,
                                    void *out, int64_t ldo, void *stream);
+
+/*
+ * int8_quant_scaled_mm_f16 - int8_quant_scaled_mm for fp16 activations x
+ * (fp16 bits, [M, ldx]): int8_quant_per_token_f16 of x, then int8_scaled_mm
+ * of the result, bit-identical to those two calls. With mode W8A8_OUT_F16
+ * (fp16 out, fp16 bias) the single-launch paths of int8_quant_scaled_mm
+ * apply; the other modes run the two steps as two launches.
+ */
+w8a8_status_t int8_quant_scaled_mm_f16(const uint16_t *x, int64_t ldx, int8_t *xq, int64_t ldq,
+                                       float *x_scale, const void *w_packed,
+                                       const float *w_scale, const uint16_t *bias, int64_t M,
+                                       int64_t N, int64_t K, int mode, void *out, int64_t ldo,
+                                       void *stream);
+
+/* int8_quant_scaled_mm_f16 with an explicit tile configuration (or -1). */
+w8a8_status_t int8_quant_scaled_mm_f16_tile(const uint16_t *x, int64_t ldx, int8_t *xq,
+                                            int64_t ldq, float *x_scale, const void *w_packed,
+                                            const float *w_scale, const uint16_t *bias,
+                                            int64_t M, int64_t N, int64_t K, int mode, void *out,
+                                            int64_t ldo, void *stream, int tile);
 
 /* int8_quant_scaled_mm with an explicit tile configuration (or -1). */
 w8a8_status_t int8_quant_scaled_mm_tile(const uint16_t *x, int64_t ldx, int8_t *xq, int64_t ldq,

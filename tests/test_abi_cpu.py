@@ -118,6 +118,27 @@ def test_prepack_validation():
     assert u(A, 16, 64, None, 64, None) == NULL
 
 
+def test_f16_entry_points_validation():
+    def q16(x=A, M=4, K=64, ldx=64, q=A, ldq=64, s=A):
+        return L.int8_quant_per_token_f16(x, M, K, ldx, q, ldq, s, None)
+    assert q16(M=-1) == SHAPE and q16(K=0) == SHAPE and q16(ldx=63) == SHAPE
+    assert q16(M=0, x=None, q=None, s=None) == OK
+    assert q16(x=None) == NULL and q16(x=A + 8) == ALIGN and q16(ldx=68) == ALIGN
+    assert q16() == DEVICE
+
+    def qm16(x=A, ldx=64, mode=2, tile=-1, **kw):
+        a = dict(xq=A, ldq=64, xs=A, wp=A, ws=A, bias=None, M=4, N=16, K=64, out=A, ldo=16)
+        a.update(kw)
+        return L.int8_quant_scaled_mm_f16_tile(x, ldx, a["xq"], a["ldq"], a["xs"], a["wp"],
+                                               a["ws"], a["bias"], a["M"], a["N"], a["K"], mode,
+                                               a["out"], a["ldo"], None, tile)
+    assert qm16(mode=3) == MODE and qm16(tile=-2) == MODE
+    assert qm16(ldx=48) == SHAPE and qm16(x=None) == NULL and qm16(x=A + 8) == ALIGN
+    assert qm16() == DEVICE and qm16(mode=0) == DEVICE and qm16(mode=1) == DEVICE
+    assert L.int8_quant_scaled_mm_f16(A, 64, A, 64, A, A, A, None, 4, 16, 64, 2, A, 16,
+                                      None) == DEVICE
+
+
 def test_quant_prepack_validation():
     def qp(w=A, dt=0, N=16, K=64, ldw=64, wp=A, ws=A):
         return L.int8_quant_prepack_weight(w, dt, N, K, ldw, wp, ws, None)
@@ -135,7 +156,8 @@ def mm(xq=A, ldq=64, xs=A, wp=A, ws=A, bias=None, M=4, N=16, K=64, mode=0, out=A
 
 
 def test_scaled_mm_validation():
-    assert mm(mode=2) == MODE and mm(mode=-1) == MODE
+    assert mm(mode=3) == MODE and mm(mode=-1) == MODE
+    assert mm(mode=2) == DEVICE and mm(mode=2, out=A + 1) == ALIGN     # fp16 out is valid
     assert mm(tile=L.w8a8_mm_tile_count()) == MODE and mm(tile=-2) == MODE
     assert mm(M=-1) == SHAPE and mm(N=0) == SHAPE
     assert mm(K=0) == SHAPE and mm(K=8) == SHAPE and mm(K=72) == SHAPE

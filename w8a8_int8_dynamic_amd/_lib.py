@@ -20,12 +20,14 @@ W8A8_ERR_MODE = 5
 W8A8_ERR_HIP = 6
 W8A8_OUT_BF16 = 0
 W8A8_OUT_I32 = 1
+W8A8_OUT_F16 = 2
 W8A8_MAX_K = 131056
 
 # name -> (restype, argtypes), in the order of include/w8a8.h
 _i64, _vp, _int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
 SIGNATURES = {
     "int8_quant_per_token": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
+    "int8_quant_per_token_f16": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
     "int8_quant_per_channel": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
     "int8_prepack_weight_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "int8_prepack_weight": (_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
@@ -39,6 +41,10 @@ SIGNATURES = {
                                     _int, _vp, _i64, _vp]),
     "int8_quant_scaled_mm_tile": (_int, [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64,
                                          _i64, _int, _vp, _i64, _vp, _int]),
+    "int8_quant_scaled_mm_f16": (_int, [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                        _int, _vp, _i64, _vp]),
+    "int8_quant_scaled_mm_f16_tile": (_int, [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64,
+                                             _i64, _int, _vp, _i64, _vp, _int]),
     "w8a8_mm_tile_count": (_int, []),
     "w8a8_mm_tile_name": (ctypes.c_char_p, [_int]),
     "w8a8_mm_tile_auto": (_int, [_i64, _i64, _i64]),

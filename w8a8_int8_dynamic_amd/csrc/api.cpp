@@ -84,9 +84,10 @@ w8a8_status_t launched(hipError_t e, const char *what)
     return ok();
 }
 
-w8a8_status_t quant_common(const void *x, bool f32, int64_t M, int64_t K, int64_t ldx, int8_t *q,
+w8a8_status_t quant_common(const void *x, int kind, int64_t M, int64_t K, int64_t ldx, int8_t *q,
                            int64_t ldq, float *s, void *stream, const char *what)
 {
+    const bool f32 = kind == w8a8::kElemF32;
     if (M < 0 || M > kMaxRows)
         return fail(W8A8_ERR_SHAPE, "%s: rows %lld out of range", what, (long long)M);
     if (K < 1 || K > kMaxRows)
@@ -108,7 +109,7 @@ w8a8_status_t quant_common(const void *x, bool f32, int64_t M, int64_t K, int64_
     w8a8_status_t st = check_device();
     if (st != W8A8_OK)
         return st;
-    return launched(w8a8::launch_quant_rows(x, f32, M, K, ldx, q, ldq, s,
+    return launched(w8a8::launch_quant_rows(x, kind, M, K, ldx, q, ldq, s,
                                             reinterpret_cast<hipStream_t>(stream)),
                     what);
 }
@@ -134,14 +135,24 @@ w8a8_status_t pack_common(int64_t N, int64_t K, int64_t ldw, const void *a, cons
 W8A8_API w8a8_status_t int8_quant_per_token(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                                             int8_t *xq, int64_t ldq, float *x_scale, void *stream)
 {
-    return quant_common(x, false, M, K, ldx, xq, ldq, x_scale, stream, "int8_quant_per_token");
+    return quant_common(x, w8a8::kElemBF16, M, K, ldx, xq, ldq, x_scale, stream,
+                        "int8_quant_per_token");
+}
+
+W8A8_API w8a8_status_t int8_quant_per_token_f16(const uint16_t *x, int64_t M, int64_t K,
+                                                int64_t ldx, int8_t *xq, int64_t ldq,
+                                                float *x_scale, void *stream)
+{
+    return quant_common(x, w8a8::kElemF16, M, K, ldx, xq, ldq, x_scale, stream,
+                        "int8_quant_per_token_f16");
 }
 
 W8A8_API w8a8_status_t int8_quant_per_channel(const float *w, int64_t N, int64_t K, int64_t ldw,
                                               int8_t *wq, int64_t ldq, float *w_scale,
                                               void *stream)
 {
-    return quant_common(w, true, N, K, ldw, wq, ldq, w_scale, stream, "int8_quant_per_channel");
+    return quant_common(w, w8a8::kElemF32, N, K, ldw, wq, ldq, w_scale, stream,
+                        "int8_quant_per_channel");
 }
 
 W8A8_API size_t int8_prepack_weight_bytes(int64_t N, int64_t K)
@@ -213,7 +224,7 @@ w8a8_status_t mm_args(const int8_t *xq, int64_t ldq, const float *x_scale, const
                       int mode, void *out, int64_t ldo, int tile, bool need_xs, const char *what,
                       w8a8::MmArgs &a, int &t)
 {
-    if (mode != W8A8_OUT_BF16 && mode != W8A8_OUT_I32)
+    if (mode != W8A8_OUT_BF16 && mode != W8A8_OUT_I32 && mode != W8A8_OUT_F16)
         return fail(W8A8_ERR_MODE, "%s: unknown output mode %d", what, mode);
     if (tile < -1 || tile >= w8a8::mm_tile_count())
         return fail(W8A8_ERR_MODE, "%s: unknown tile %d", what, tile);
@@ -252,7 +263,7 @@ w8a8_status_t mm_args(const int8_t *xq, int64_t ldq, const float *x_scale, const
     a.K = (int)K;
     a.kblocks = (int)w8a8::ceil_div(K, w8a8::kFragK);
     a.nblocks = (int)w8a8::ceil_div(N, w8a8::kFragN);
-    // 8-byte bf16 / 16-byte int32 stores of 4 consecutive channels need every
+    // 8-byte 16-bit / 16-byte int32 stores of 4 consecutive channels need every
     // row start (and channel multiples of 4) aligned to that width.
     const uintptr_t vw = 4 * esz;
     a.vec_store = aligned(out, vw) && ((uint64_t)ldo * esz) % vw == 0;
@@ -279,19 +290,18 @@ W8A8_API w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const 
     st = check_device();
     if (st != W8A8_OK)
         return st;
-    return launched(w8a8::launch_scaled_mm(a, mode == W8A8_OUT_I32, t,
-                                           reinterpret_cast<hipStream_t>(stream)),
+    return launched(w8a8::launch_scaled_mm(a, mode, t, reinterpret_cast<hipStream_t>(stream)),
                     what);
 }
 
-W8A8_API w8a8_status_t int8_quant_scaled_mm_tile(const uint16_t *x, int64_t ldx, int8_t *xq,
-                                                 int64_t ldq, float *x_scale,
-                                                 const void *w_packed, const float *w_scale,
-                                                 const uint16_t *bias, int64_t M, int64_t N,
-                                                 int64_t K, int mode, void *out, int64_t ldo,
-                                                 void *stream, int tile)
+namespace {
+
+// The fused entry points for bf16 and fp16 activations (x_kind).
+w8a8_status_t quant_mm_common(const uint16_t *x, int x_kind, int64_t ldx, int8_t *xq, int64_t ldq,
+                              float *x_scale, const void *w_packed, const float *w_scale,
+                              const uint16_t *bias, int64_t M, int64_t N, int64_t K, int mode,
+                              void *out, int64_t ldo, void *stream, int tile, const char *what)
 {
-    const char *what = "int8_quant_scaled_mm";
     w8a8::MmArgs a;
     int t;
     w8a8_status_t st = mm_args(xq, ldq, x_scale, w_packed, w_scale, bias, M, N, K, mode, out, ldo,
@@ -309,21 +319,59 @@ W8A8_API w8a8_status_t int8_quant_scaled_mm_tile(const uint16_t *x, int64_t ldx,
     st = check_device();
     if (st != W8A8_OK)
         return st;
-    const bool i32 = mode == W8A8_OUT_I32;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     a.x = x;
     a.ldx = ldx;
-    hipError_t err = w8a8::launch_quant_scaled_mm(a, i32, t, s);
-    if (err != hipErrorNotSupported)
-        return launched(err, what);
-    // The grid cannot be resident all at once: run the two steps as two
-    // launches on the same stream.
-    (void)hipGetLastError();
+    // The single-launch kernels read x in the output's 16-bit type (bf16 for
+    // the int32 mode); other pairings take the two launches.
+    const int fused_kind = mode == W8A8_OUT_F16 ? w8a8::kElemF16 : w8a8::kElemBF16;
+    if (x_kind == fused_kind) {
+        hipError_t err = w8a8::launch_quant_scaled_mm(a, mode, t, s);
+        if (err != hipErrorNotSupported)
+            return launched(err, what);
+        (void)hipGetLastError();
+    }
+    // Two launches on the same stream (also when the grid cannot be
+    // resident all at once).
     a.x = nullptr;
-    err = w8a8::launch_quant_rows(x, false, M, K, ldx, xq, ldq, x_scale, s);
+    hipError_t err = w8a8::launch_quant_rows(x, x_kind, M, K, ldx, xq, ldq, x_scale, s);
     if (err != hipSuccess)
         return launched(err, what);
-    return launched(w8a8::launch_scaled_mm(a, i32, t, s), what);
+    return launched(w8a8::launch_scaled_mm(a, mode, t, s), what);
+}
+
+}  // namespace
+
+W8A8_API w8a8_status_t int8_quant_scaled_mm_tile(const uint16_t *x, int64_t ldx, int8_t *xq,
+                                                 int64_t ldq, float *x_scale,
+                                                 const void *w_packed, const float *w_scale,
+                                                 const uint16_t *bias, int64_t M, int64_t N,
+                                                 int64_t K, int mode, void *out, int64_t ldo,
+                                                 void *stream, int tile)
+{
+    return quant_mm_common(x, w8a8::kElemBF16, ldx, xq, ldq, x_scale, w_packed, w_scale, bias, M, N,
+                           K, mode, out, ldo, stream, tile, "int8_quant_scaled_mm");
+}
+
+W8A8_API w8a8_status_t int8_quant_scaled_mm_f16_tile(const uint16_t *x, int64_t ldx, int8_t *xq,
+                                                     int64_t ldq, float *x_scale,
+                                                     const void *w_packed, const float *w_scale,
+                                                     const uint16_t *bias, int64_t M, int64_t N,
+                                                     int64_t K, int mode, void *out, int64_t ldo,
+                                                     void *stream, int tile)
+{
+    return quant_mm_common(x, w8a8::kElemF16, ldx, xq, ldq, x_scale, w_packed, w_scale, bias, M, N,
+                           K, mode, out, ldo, stream, tile, "int8_quant_scaled_mm_f16");
+}
+
+W8A8_API w8a8_status_t int8_quant_scaled_mm_f16(const uint16_t *x, int64_t ldx, int8_t *xq,
+                                                int64_t ldq, float *x_scale, const void *w_packed,
+                                                const float *w_scale, const uint16_t *bias,
+                                                int64_t M, int64_t N, int64_t K, int mode,
+                                                void *out, int64_t ldo, void *stream)
+{
+    return int8_quant_scaled_mm_f16_tile(x, ldx, xq, ldq, x_scale, w_packed, w_scale, bias, M, N,
+                                         K, mode, out, ldo, stream, -1);
 }
 
 W8A8_API w8a8_status_t int8_quant_scaled_mm(const uint16_t *x, int64_t ldx, int8_t *xq,

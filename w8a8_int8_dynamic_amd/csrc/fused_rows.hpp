@@ -45,7 +45,7 @@ constexpr int kSpinLimit = 1 << 12;
 // per lane, 8 / CPL rows per wavefront in flight (all their loads issued
 // before the first reduction); the reduction stays inside the wavefront, so
 // there is no barrier. Wave w takes row groups w, w + NW, ... of [ra, rb).
-template <int THREADS, int CPL>
+template <int THREADS, int CPL, int E>
 __device__ __forceinline__ void quantize_rows_by_wave(const MmArgs &a, int ra, int rb)
 {
     using namespace quant_rule;
@@ -71,17 +71,17 @@ __device__ __forceinline__ void quantize_rows_by_wave(const MmArgs &a, int ra, i
             u32 mx = 0;
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
-                mx = max(mx, chunk_absmax<false>(v[i][c]));
+                mx = max(mx, chunk_absmax<E>(v[i][c]));
             mx = wave_max(mx);
             float sc, inv;
-            scale_of(mx, false, sc, inv);
+            scale_of(mx, E, sc, inv);
             int8_t *qrow = const_cast<int8_t *>(a.xq) + (int64_t)(g + i) * a.ldq;
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 const int e = (c * 64 + lane) * 8;
                 if (e < a.K) {
                     u32 lo, hi;
-                    chunk_codes<false>(v[i][c], inv, lo, hi);
+                    chunk_codes<E>(v[i][c], inv, lo, hi);
                     __hip_atomic_store(reinterpret_cast<uint64_t *>(qrow + e), (uint64_t)hi << 32 | lo,
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
@@ -93,32 +93,33 @@ __device__ __forceinline__ void quantize_rows_by_wave(const MmArgs &a, int ra, i
     }
 }
 
-// Rows [ra, rb) of x (bf16 [M, ldx]) into xq / xs by the THREADS threads of
-// a workgroup, with the rule of int8_quant_per_token. Rows of up to 4096
+// Rows [ra, rb) of x (16-bit floats of kind E, bf16 or fp16, [M, ldx]) into
+// xq / xs by the THREADS threads of a workgroup, with the rule of
+// int8_quant_per_token. Rows of up to 4096
 // elements go one per wavefront (quantize_rows_by_wave). Longer rows use the
 // whole workgroup: a row of up to 8 * 8 * THREADS elements is held in
 // registers (one read of x; two such rows at a time when they fit); longer
 // still take an absmax pass and a codes pass that re-reads the row from L2.
 // red: 2 * THREADS / 64 words of LDS. Every thread of the workgroup must
 // call this (it may hold barriers).
-template <int THREADS>
+template <int THREADS, int E>
 __device__ __forceinline__ void quantize_rows(const MmArgs &a, int ra, int rb, u32 *red)
 {
     using namespace quant_rule;
     if (a.K <= 64 * 8) {
-        quantize_rows_by_wave<THREADS, 1>(a, ra, rb);
+        quantize_rows_by_wave<THREADS, 1, E>(a, ra, rb);
         return;
     }
     if (a.K <= 64 * 8 * 2) {
-        quantize_rows_by_wave<THREADS, 2>(a, ra, rb);
+        quantize_rows_by_wave<THREADS, 2, E>(a, ra, rb);
         return;
     }
     if (a.K <= 64 * 8 * 4) {
-        quantize_rows_by_wave<THREADS, 4>(a, ra, rb);
+        quantize_rows_by_wave<THREADS, 4, E>(a, ra, rb);
         return;
     }
     if (a.K <= 64 * 8 * 8 && rb - ra > THREADS / 64) {
-        quantize_rows_by_wave<THREADS, 8>(a, ra, rb);
+        quantize_rows_by_wave<THREADS, 8, E>(a, ra, rb);
         return;
     }
     constexpr int NW = THREADS / 64;
@@ -148,7 +149,7 @@ __device__ __forceinline__ void quantize_rows(const MmArgs &a, int ra, int rb, u
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
                 const int e = (c * THREADS + (int)threadIdx.x) * 8;
-                v[k][c] = e < a.K ? load_chunk<false>(xrow, e, a.K) : make_uint4(0, 0, 0, 0);
+                v[k][c] = e < a.K ? load_chunk<E>(xrow, e, a.K) : make_uint4(0, 0, 0, 0);
             }
         }
 #pragma unroll
@@ -156,7 +157,7 @@ __device__ __forceinline__ void quantize_rows(const MmArgs &a, int ra, int rb, u
             mx[k] = 0;
 #pragma unroll
             for (int c = 0; c < CH; ++c)
-                mx[k] = max(mx[k], chunk_absmax<false>(v[k][c]));
+                mx[k] = max(mx[k], chunk_absmax<E>(v[k][c]));
             mx[k] = wave_max(mx[k]);
             if (lane == 0)
                 red[k * NW + wave] = mx[k];
@@ -171,14 +172,14 @@ __device__ __forceinline__ void quantize_rows(const MmArgs &a, int ra, int rb, u
 #pragma unroll
         for (int k = 0; k < NR; ++k) {
             float sc, inv;
-            scale_of(mx[k], false, sc, inv);
+            scale_of(mx[k], E, sc, inv);
             int8_t *qrow = const_cast<int8_t *>(a.xq) + (int64_t)(r + k) * a.ldq;
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
                 const int e = (c * THREADS + (int)threadIdx.x) * 8;
                 if (e < a.K) {
                     u32 lo, hi;
-                    chunk_codes<false>(v[k][c], inv, lo, hi);
+                    chunk_codes<E>(v[k][c], inv, lo, hi);
                     put_codes(qrow, e, lo, hi);
                 }
             }
@@ -190,7 +191,7 @@ __device__ __forceinline__ void quantize_rows(const MmArgs &a, int ra, int rb, u
         int8_t *qrow = const_cast<int8_t *>(a.xq) + (int64_t)r * a.ldq;
         u32 mx = 0;
         for (int e = (int)threadIdx.x * 8; e < a.K; e += THREADS * 8)
-            mx = max(mx, chunk_absmax<false>(load_chunk<false>(xrow, e, a.K)));
+            mx = max(mx, chunk_absmax<E>(load_chunk<E>(xrow, e, a.K)));
         mx = wave_max(mx);
         if (lane == 0)
             red[wave] = mx;
@@ -200,10 +201,10 @@ __device__ __forceinline__ void quantize_rows(const MmArgs &a, int ra, int rb, u
             mx = max(mx, red[w]);
         __syncthreads();
         float sc, inv;
-        scale_of(mx, false, sc, inv);
+        scale_of(mx, E, sc, inv);
         for (int e = (int)threadIdx.x * 8; e < a.K; e += THREADS * 8) {
             u32 lo, hi;
-            chunk_codes<false>(load_chunk<false>(xrow, e, a.K), inv, lo, hi);
+            chunk_codes<E>(load_chunk<E>(xrow, e, a.K), inv, lo, hi);
             put_codes(qrow, e, lo, hi);
         }
         put_scale(r, sc);

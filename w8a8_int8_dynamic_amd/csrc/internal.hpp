@@ -15,9 +15,12 @@ constexpr int kFragBytes = 1024;
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
+// Element kinds of rows and outputs (the quant rule's kBF16 / kF32 / kF16).
+constexpr int kElemBF16 = 0, kElemF32 = 1, kElemF16 = 2;
+
 // ---- per-row quantization (quant.hip) ----
-// in_f32 = false: x is bf16 bits [rows, ldx]; true: x is fp32 [rows, ldx].
-hipError_t launch_quant_rows(const void *x, bool in_f32, int64_t rows, int64_t K, int64_t ldx,
+// kind: x is bf16 bits, fp32 or fp16 bits [rows, ldx].
+hipError_t launch_quant_rows(const void *x, int kind, int64_t rows, int64_t K, int64_t ldx,
                              int8_t *q, int64_t ldq, float *scale, hipStream_t stream);
 
 // ---- weight repack (prepack.hip) ----
@@ -53,15 +56,19 @@ struct MmArgs {
     unsigned epoch;  // this launch's number on its device, never 0
 };
 
+// Output kinds, the ABI's W8A8_OUT_* values: they index TileEntry's kernels.
+constexpr int kOutBF16 = 0, kOutI32 = 1, kOutF16 = 2, kOutKinds = 3;
+
 // One tile configuration: its output tile (bm x bn), block size and
-// kernels (bf16 and int32 output; the fused quant + matmul forms, or null
-// where the configuration has none). skinny marks the small-M kernel.
+// kernels per output kind (plain, and the fused quant + matmul forms, which
+// read x in the output's 16-bit type, bf16 for int32; null where the
+// configuration has none). skinny marks the small-M kernel.
 typedef void (*MmKernel)(const MmArgs);
 struct TileEntry {
     const char *name;
     int bm, bn, threads;
     bool skinny;
-    MmKernel bf16, i32, bf16_fused, i32_fused;
+    MmKernel plain[kOutKinds], fused[kOutKinds];
 };
 
 // Small-M configurations (skinny_mm.hip); they follow the main kernel's in
@@ -70,7 +77,7 @@ int skinny_tile_count();
 const TileEntry &skinny_tile(int i);
 // Fused quant + small-M matmul (each workgroup quantizes its own rows);
 // hipErrorNotSupported (nothing launched) when the rows are too long.
-hipError_t launch_skinny_quant_mm(const MmArgs &a, const TileEntry &e, bool out_i32,
+hipError_t launch_skinny_quant_mm(const MmArgs &a, const TileEntry &e, int mode,
                                   hipStream_t stream);
 
 // Physical workgroup id -> logical tile id such that each XCD (which takes
@@ -86,10 +93,10 @@ __device__ __forceinline__ int xcd_remap(int pid, int tiles)
 int mm_tile_count();
 const char *mm_tile_name(int tile);
 int mm_tile_auto(int64_t M, int64_t N, int64_t K);
-hipError_t launch_scaled_mm(const MmArgs &a, bool out_i32, int tile, hipStream_t stream);
+hipError_t launch_scaled_mm(const MmArgs &a, int mode, int tile, hipStream_t stream);
 // Fused quant + matmul in one launch. Returns hipErrorNotSupported (nothing
 // launched) when the shape's workgroups cannot all be resident at once; the
 // caller then runs the two steps as separate launches.
-hipError_t launch_quant_scaled_mm(MmArgs a, bool out_i32, int tile, hipStream_t stream);
+hipError_t launch_quant_scaled_mm(MmArgs a, int mode, int tile, hipStream_t stream);
 
 }  // namespace w8a8

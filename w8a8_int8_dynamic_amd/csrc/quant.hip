@@ -1,8 +1,9 @@
 // Per-row symmetric int8 quantization on gfx950.
 //
 // One kernel family serves two steps of the layer: the dynamic per-token
-// activation quant (bf16 rows; page "Issue 5 probe: int8 quantized DiT serve
-// paths on the RTX 3090 (24 GB)", section "Round two") and the
+// activation quant (bf16 or fp16 rows; page "Issue 5 probe: int8 quantized
+// DiT serve paths on the RTX 3090 (24 GB)", section "Round two", and the
+// isolation table's bf16 and fp16 activation columns) and the
 // per-output-channel weight quant (fp32 rows; same page, "Round one" setup
 // and "Round two" artifacts paragraphs). The rule per row:
 //   a = max |x|;  a < 2^-100 -> scale 0, codes 0;
@@ -19,7 +20,7 @@
 //     order like the values; a wavefront reduces with DPP (quad_perm,
 //     row_half_mirror, row_mirror) and four readlanes; the WPR partials of
 //     a row meet in LDS.
-//   - Codes are written 8 (bf16) or 4 (fp32) per lane per chunk.
+//   - Codes are written 8 (bf16, fp16) or 4 (fp32) per lane per chunk.
 //   - The row loads of the single-pass kernel and all code stores are
 //     nontemporal: each byte is touched once, and keeping it out of the
 //     caches lifts HBM throughput.
@@ -36,13 +37,13 @@ namespace {
 using namespace quant_rule;
 
 // Register-resident kernel: CH chunks per lane, WPR waves per row, 4 waves per block.
-template <bool F32, int CH, int WPR>
+template <int E, int CH, int WPR>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void *__restrict__ x, int64_t rows,
                                                          int K, int64_t ldx,
                                                          int8_t *__restrict__ q, int64_t ldq,
                                                          float *__restrict__ scale)
 {
-    constexpr int VEC = Elem<F32>::VEC;
+    constexpr int VEC = Elem<E>::VEC;
     constexpr int RPB = 4 / WPR;
     __shared__ u32 part[4];
     const int lane = threadIdx.x & 63;
@@ -50,18 +51,18 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void *__restrict_
     const int wr = wave % WPR;
     const int64_t row = (int64_t)blockIdx.x * RPB + wave / WPR;
     const bool valid = row < rows;
-    const char *xrow = reinterpret_cast<const char *>(x) + row * ldx * Elem<F32>::BYTES;
+    const char *xrow = reinterpret_cast<const char *>(x) + row * ldx * Elem<E>::BYTES;
 
     uint4 v[CH];
     u32 m = 0;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int64_t e = ((int64_t)(c * WPR + wr) * 64 + lane) * VEC;
-        v[c] = (valid && e < K) ? load_chunk<F32, true>(xrow, e, K) : make_uint4(0, 0, 0, 0);
+        v[c] = (valid && e < K) ? load_chunk<E, true>(xrow, e, K) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int c = 0; c < CH; ++c)
-        m = max(m, chunk_absmax<F32>(v[c]));
+        m = max(m, chunk_absmax<E>(v[c]));
     m = wave_max(m);
     if (WPR > 1) {
         if (lane == 0)
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void *__restrict_
     if (!valid)
         return;
     float s, inv;
-    scale_of(m, F32, s, inv);
+    scale_of(m, E, s, inv);
     if (wr == 0 && lane == 0)
         scale[row] = s;
     int8_t *qrow = q + row * ldq;
@@ -85,44 +86,44 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void *__restrict_
         const int64_t e = ((int64_t)(c * WPR + wr) * 64 + lane) * VEC;
         if (e < K) {
             u32 lo, hi;
-            chunk_codes<F32>(v[c], inv, lo, hi);
-            store_codes<F32>(qrow, e, K, lo, hi);
+            chunk_codes<E>(v[c], inv, lo, hi);
+            store_codes<E>(qrow, e, K, lo, hi);
         }
     }
 }
 
 // Two-pass kernel for rows longer than the register-resident limit:
 // one row per block of 4 waves; pass 1 finds the absmax, pass 2 re-reads.
-template <bool F32>
+template <int E>
 __global__ __launch_bounds__(256) void quant_rows_looped_kernel(const void *__restrict__ x,
                                                                 int64_t rows, int K, int64_t ldx,
                                                                 int8_t *__restrict__ q, int64_t ldq,
                                                                 float *__restrict__ scale)
 {
-    constexpr int VEC = Elem<F32>::VEC;
+    constexpr int VEC = Elem<E>::VEC;
     __shared__ u32 part[4];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t row = blockIdx.x;
-    const char *xrow = reinterpret_cast<const char *>(x) + row * ldx * Elem<F32>::BYTES;
+    const char *xrow = reinterpret_cast<const char *>(x) + row * ldx * Elem<E>::BYTES;
     const int64_t step = 256 * VEC;
     u32 m = 0;
     for (int64_t e = (int64_t)threadIdx.x * VEC; e < K; e += step)
-        m = max(m, chunk_absmax<F32>(load_chunk<F32>(xrow, e, K)));
+        m = max(m, chunk_absmax<E>(load_chunk<E>(xrow, e, K)));
     m = wave_max(m);
     if (lane == 0)
         part[wave] = m;
     __syncthreads();
     m = max(max(part[0], part[1]), max(part[2], part[3]));
     float s, inv;
-    scale_of(m, F32, s, inv);
+    scale_of(m, E, s, inv);
     if (threadIdx.x == 0)
         scale[row] = s;
     int8_t *qrow = q + row * ldq;
     for (int64_t e = (int64_t)threadIdx.x * VEC; e < K; e += step) {
         u32 lo, hi;
-        chunk_codes<F32>(load_chunk<F32>(xrow, e, K), inv, lo, hi);
-        store_codes<F32>(qrow, e, K, lo, hi);
+        chunk_codes<E>(load_chunk<E>(xrow, e, K), inv, lo, hi);
+        store_codes<E>(qrow, e, K, lo, hi);
     }
 }
 
@@ -132,39 +133,39 @@ constexpr int kChOptions[] = {1, 2, 3, 4, 6, 8, 12, 16};
 constexpr int kNumCh = sizeof(kChOptions) / sizeof(kChOptions[0]);
 constexpr int kWprOptions[] = {1, 2, 4};
 
-template <bool F32, int WPR>
+template <int E, int WPR>
 QuantFn pick_ch(int idx)
 {
     switch (idx) {
-    case 0: return quant_rows_kernel<F32, 1, WPR>;
-    case 1: return quant_rows_kernel<F32, 2, WPR>;
-    case 2: return quant_rows_kernel<F32, 3, WPR>;
-    case 3: return quant_rows_kernel<F32, 4, WPR>;
-    case 4: return quant_rows_kernel<F32, 6, WPR>;
-    case 5: return quant_rows_kernel<F32, 8, WPR>;
-    case 6: return quant_rows_kernel<F32, 12, WPR>;
-    default: return quant_rows_kernel<F32, 16, WPR>;
+    case 0: return quant_rows_kernel<E, 1, WPR>;
+    case 1: return quant_rows_kernel<E, 2, WPR>;
+    case 2: return quant_rows_kernel<E, 3, WPR>;
+    case 3: return quant_rows_kernel<E, 4, WPR>;
+    case 4: return quant_rows_kernel<E, 6, WPR>;
+    case 5: return quant_rows_kernel<E, 8, WPR>;
+    case 6: return quant_rows_kernel<E, 12, WPR>;
+    default: return quant_rows_kernel<E, 16, WPR>;
     }
 }
 
-template <bool F32>
+template <int E>
 QuantFn pick(int wpr, int ch_idx)
 {
     switch (wpr) {
-    case 1: return pick_ch<F32, 1>(ch_idx);
-    case 2: return pick_ch<F32, 2>(ch_idx);
-    default: return pick_ch<F32, 4>(ch_idx);
+    case 1: return pick_ch<E, 1>(ch_idx);
+    case 2: return pick_ch<E, 2>(ch_idx);
+    default: return pick_ch<E, 4>(ch_idx);
     }
 }
 
 }  // namespace
 
-hipError_t launch_quant_rows(const void *x, bool in_f32, int64_t rows, int64_t K, int64_t ldx,
+hipError_t launch_quant_rows(const void *x, int kind, int64_t rows, int64_t K, int64_t ldx,
                              int8_t *q, int64_t ldq, float *scale, hipStream_t stream)
 {
     if (rows == 0)
         return hipSuccess;
-    const int vec = in_f32 ? 4 : 8;
+    const int vec = kind == kF32 ? 4 : 8;
     const int64_t chunks = ceil_div(K, vec);
     // Fewest waves per row that keep the row in registers, unless the grid
     // would then have too few waves to cover the machine's latency.
@@ -183,17 +184,16 @@ hipError_t launch_quant_rows(const void *x, bool in_f32, int64_t rows, int64_t K
         if (wpr < 4 && need > 1 && rows * wpr < kEnoughWaves)
             continue;
         const int rpb = 4 / wpr;
-        QuantFn fn = in_f32 ? pick<true>(wpr, ch_idx) : pick<false>(wpr, ch_idx);
+        QuantFn fn = kind == kF32 ? pick<kF32>(wpr, ch_idx)
+                   : kind == kF16 ? pick<kF16>(wpr, ch_idx) : pick<kBF16>(wpr, ch_idx);
         hipLaunchKernelGGL(fn, dim3((unsigned)ceil_div(rows, rpb)), dim3(256), 0, stream, x, rows,
                            (int)K, ldx, q, ldq, scale);
         return hipGetLastError();
     }
-    if (in_f32)
-        hipLaunchKernelGGL(quant_rows_looped_kernel<true>, dim3((unsigned)rows), dim3(256), 0,
-                           stream, x, rows, (int)K, ldx, q, ldq, scale);
-    else
-        hipLaunchKernelGGL(quant_rows_looped_kernel<false>, dim3((unsigned)rows), dim3(256), 0,
-                           stream, x, rows, (int)K, ldx, q, ldq, scale);
+    QuantFn fn = kind == kF32 ? quant_rows_looped_kernel<kF32>
+               : kind == kF16 ? quant_rows_looped_kernel<kF16> : quant_rows_looped_kernel<kBF16>;
+    hipLaunchKernelGGL(fn, dim3((unsigned)rows), dim3(256), 0, stream, x, rows, (int)K, ldx, q,
+                       ldq, scale);
     return hipGetLastError();
 }
 

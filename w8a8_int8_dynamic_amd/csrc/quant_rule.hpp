@@ -1,7 +1,10 @@
 // The per-row symmetric int8 quantization rule, shared by the quant kernels
 // and the fused quant + matmul path so that both produce the same codes bit
 // for bit (page "Issue 5 probe: int8 quantized DiT serve paths on the RTX
-// 3090 (24 GB)", section "Round two": dynamic per-token symmetric int8):
+// 3090 (24 GB)", section "Round two": dynamic per-token symmetric int8).
+// Rows are bf16, fp32 or fp16 (element kinds kBF16, kF32, kF16; a bool
+// template argument false / true still means bf16 / fp32); every element is
+// widened to fp32 exactly first:
 //   a = max |x|;  a < 2^-100 -> scale 0, codes 0;
 //   else scale = fl32(a/127), inv = fl32(127/a),
 //        q = clamp(rint_even(fl32(x*inv)), -127, 127).
@@ -33,16 +36,27 @@ __device__ __forceinline__ u32 wave_max(u32 v)
     return max(max(r0, r1), max(r2, r3));
 }
 
-template <bool F32>
+constexpr int kBF16 = 0, kF32 = 1, kF16 = 2;
+
+template <int E>
 struct Elem {
+    static constexpr bool F32 = E == kF32;
     static constexpr int VEC = F32 ? 4 : 8;       // elements per 16-byte chunk
     static constexpr int BYTES = F32 ? 4 : 2;
 };
 
-// Largest |x| bit pattern in one chunk.
-template <bool F32>
+// fp16 bits (low 16 bits of h) -> fp32, exact.
+__device__ __forceinline__ float f16_to_float(u32 h)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xffffu));
+}
+
+// Largest |x| bit pattern in one chunk (for bf16 and fp16 alike the 15 low
+// bits of a 16-bit value order magnitudes).
+template <int E>
 __device__ __forceinline__ u32 chunk_absmax(const uint4 &v)
 {
+    constexpr bool F32 = E == kF32;
     const u32 d[4] = {v.x, v.y, v.z, v.w};
     u32 m = 0;
 #pragma unroll
@@ -64,12 +78,13 @@ __device__ __forceinline__ u32 code(float f, float inv)
     return (u32)((int)t) & 0xffu;
 }
 
-// Codes of one chunk: bf16 -> 8 codes in (lo, hi); fp32 -> 4 codes in lo.
-template <bool F32>
+// Codes of one chunk: bf16 or fp16 -> 8 codes in (lo, hi); fp32 -> 4 codes
+// in lo.
+template <int E>
 __device__ __forceinline__ void chunk_codes(const uint4 &v, float inv, u32 &lo, u32 &hi)
 {
     const u32 d[4] = {v.x, v.y, v.z, v.w};
-    if (F32) {
+    if (E == kF32) {
         lo = code(__uint_as_float(d[0]), inv) | code(__uint_as_float(d[1]), inv) << 8 |
              code(__uint_as_float(d[2]), inv) << 16 | code(__uint_as_float(d[3]), inv) << 24;
         hi = 0;
@@ -77,8 +92,13 @@ __device__ __forceinline__ void chunk_codes(const uint4 &v, float inv, u32 &lo, 
         u32 c[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            c[2 * i] = code(__uint_as_float(d[i] << 16), inv);
-            c[2 * i + 1] = code(__uint_as_float(d[i] & 0xffff0000u), inv);
+            if (E == kF16) {
+                c[2 * i] = code(f16_to_float(d[i]), inv);
+                c[2 * i + 1] = code(f16_to_float(d[i] >> 16), inv);
+            } else {
+                c[2 * i] = code(__uint_as_float(d[i] << 16), inv);
+                c[2 * i + 1] = code(__uint_as_float(d[i] & 0xffff0000u), inv);
+            }
         }
         lo = c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24;
         hi = c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24;
@@ -89,11 +109,12 @@ __device__ __forceinline__ void chunk_codes(const uint4 &v, float inv, u32 &lo, 
 // marks the data as read once (nontemporal: it is not kept in the caches),
 // which the single-pass kernel uses; measured on MI355X this raises the
 // quant's HBM throughput by about 14 % on 300 MB passes.
-template <bool F32, bool STREAM = false>
+template <int E, bool STREAM = false>
 __device__ __forceinline__ uint4 load_chunk(const char *row, int64_t e, int K)
 {
-    constexpr int VEC = Elem<F32>::VEC;
-    constexpr int B = Elem<F32>::BYTES;
+    constexpr bool F32 = E == kF32;
+    constexpr int VEC = Elem<E>::VEC;
+    constexpr int B = Elem<E>::BYTES;
     if (e + VEC <= K) {
         if (STREAM) {
             const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(row + e * B));
@@ -113,10 +134,11 @@ __device__ __forceinline__ uint4 load_chunk(const char *row, int64_t e, int K)
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-template <bool F32>
+template <int E>
 __device__ __forceinline__ void store_codes(int8_t *qrow, int64_t e, int K, u32 lo, u32 hi)
 {
-    constexpr int VEC = Elem<F32>::VEC;
+    constexpr bool F32 = E == kF32;
+    constexpr int VEC = Elem<E>::VEC;
     if (e + VEC <= K) {
         // The codes are not read again by this pass: stream them out.
         if (F32)
@@ -130,9 +152,10 @@ __device__ __forceinline__ void store_codes(int8_t *qrow, int64_t e, int K, u32 
             qrow[e + j] = (int8_t)((j < 4 ? lo >> (8 * j) : hi >> (8 * (j - 4))) & 0xffu);
 }
 
-__device__ __forceinline__ void scale_of(u32 m, bool f32, float &s, float &inv)
+// Scale and reciprocal of a row from its absmax bit pattern m (kind e).
+__device__ __forceinline__ void scale_of(u32 m, int e, float &s, float &inv)
 {
-    const float a = __uint_as_float(f32 ? m : m << 16);
+    const float a = e == kF32 ? __uint_as_float(m) : e == kF16 ? f16_to_float(m) : __uint_as_float(m << 16);
     if (a < 0x1p-100f) {
         s = 0.0f;
         inv = 0.0f;                      // x * 0 -> code 0 for every element

@@ -65,6 +65,22 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Four fp32 values rounded to nearest-even 16-bit floats (fp16 when F16,
+// else bf16), packed in order into two words.
+template <bool F16>
+__device__ __forceinline__ v2u pack4(const float (&t)[4])
+{
+    if (F16) {
+        const f16x2 lo = __builtin_convertvector((f32x2){t[0], t[1]}, f16x2);
+        const f16x2 hi = __builtin_convertvector((f32x2){t[2], t[3]}, f16x2);
+        return v2u{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+    }
+    const bf16x2 lo = __builtin_convertvector((f32x2){t[0], t[1]}, bf16x2);
+    const bf16x2 hi = __builtin_convertvector((f32x2){t[2], t[3]}, bf16x2);
+    return v2u{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+}
 
 // Logical tile id -> (tm, tn): bands of kBandM M-tiles; inside a band the
 // M index runs fastest. The 32 tiles an XCD runs at once then form a block
@@ -176,9 +192,13 @@ struct Tile {
     static_assert(WK <= 2 && FM % WK == 0, "k-groups split the row tiles evenly");
 };
 
-template <class T, bool OUT_I32, bool FUSED>
+// OUT: kOutBF16, kOutI32 or kOutF16. The fused form reads x in the output's
+// 16-bit type (bf16 for the int32 debug mode).
+template <class T, int OUT, bool FUSED>
 __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args)
 {
+    constexpr bool OUT_I32 = OUT == kOutI32, OUT_F16 = OUT == kOutF16;
+    constexpr int IN = OUT_F16 ? kElemF16 : kElemBF16;
     __shared__ uint4 lds[T::LDS / 16];
 
     MmArgs a;
@@ -374,12 +394,12 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
             reinterpret_cast<quant_rule::u32 *>(reinterpret_cast<char *>(lds) + T::FLAG);
         const int r0 = (int)blockIdx.x * a.rows_per_wg;
         const int r1 = min(r0 + a.rows_per_wg, a.M);
-        fused::quantize_rows<T::THREADS>(a, r0, r1, red);
+        fused::quantize_rows<T::THREADS, IN>(a, r0, r1, red);
         fused::publish(a, r0 < r1);
         const int rows = min(T::BM, a.M - m0);
         const int producers = (rows + a.rows_per_wg - 1) / a.rows_per_wg;
         if (fused::wait_producers(a, m0 / a.rows_per_wg, producers, decision)) {
-            fused::quantize_rows<T::THREADS>(a, m0, m0 + rows, red);
+            fused::quantize_rows<T::THREADS, IN>(a, m0, m0 + rows, red);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
@@ -399,8 +419,10 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
             if (p < T::BN)
                 v = a.ws[min(n0 + p, a.N - 1)];
             else if (p < 2 * T::BN) {
-                if (a.bias)
-                    v = __uint_as_float((unsigned)a.bias[min(n0 + p - T::BN, a.N - 1)] << 16);
+                if (a.bias) {
+                    const unsigned b = a.bias[min(n0 + p - T::BN, a.N - 1)];
+                    v = OUT_F16 ? quant_rule::f16_to_float(b) : __uint_as_float(b << 16);
+                }
             } else if (p < T::SIDE)
                 v = a.xs[min(m0 + p - 2 * T::BN, a.M - 1)];
             side_v[u] = v;
@@ -568,10 +590,8 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
                             if (B)
                                 t[r] = t[r] + b4[r];
                         }
-                        const bf16x2 lo = __builtin_convertvector((f32x2){t[0], t[1]}, bf16x2);
-                        const bf16x2 hi = __builtin_convertvector((f32x2){t[2], t[3]}, bf16x2);
                         *reinterpret_cast<v2u *>(tile_lds + ml * T::PITCH + nl * 2) =
-                            v2u{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+                            pack4<OUT_F16>(t);
                     }
             }
         };
@@ -635,9 +655,11 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
 template <class T>
 constexpr TileEntry entry(const char *name)
 {
-    return TileEntry{name, T::BM, T::BN, T::THREADS, false, scaled_mm_kernel<T, false, false>,
-                     scaled_mm_kernel<T, true, false>, scaled_mm_kernel<T, false, true>,
-                     scaled_mm_kernel<T, true, true>};
+    return TileEntry{name, T::BM, T::BN, T::THREADS, false,
+                     {scaled_mm_kernel<T, kOutBF16, false>, scaled_mm_kernel<T, kOutI32, false>,
+                      scaled_mm_kernel<T, kOutF16, false>},
+                     {scaled_mm_kernel<T, kOutBF16, true>, scaled_mm_kernel<T, kOutI32, true>,
+                      scaled_mm_kernel<T, kOutF16, true>}};
 }
 
 // BM x BN output tile / WM row groups x WN column groups x WK k-groups of
@@ -713,12 +735,12 @@ int mm_tile_auto(int64_t M, int64_t N, int64_t K)
     return best;
 }
 
-hipError_t launch_scaled_mm(const MmArgs &a, bool out_i32, int tile, hipStream_t stream)
+hipError_t launch_scaled_mm(const MmArgs &a, int mode, int tile, hipStream_t stream)
 {
     const TileEntry &e = tile_entry(tile);
     const int64_t tiles = ceil_div(a.M, e.bm) * ceil_div(a.N, e.bn);
     const int threads = e.threads;
-    hipLaunchKernelGGL(out_i32 ? e.i32 : e.bf16, dim3((unsigned)tiles), dim3(threads), 0, stream, a);
+    hipLaunchKernelGGL(e.plain[mode], dim3((unsigned)tiles), dim3(threads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -727,12 +749,12 @@ hipError_t launch_scaled_mm(const MmArgs &a, bool out_i32, int tile, hipStream_t
 // runtime's occupancy query costs tens of microseconds, far more than the
 // small launches this path serves, so it runs once.
 constexpr int kCapDevices = 64, kCapTiles = 32;
-static std::atomic<int> g_capacity[kCapDevices][kCapTiles][2];
+static std::atomic<int> g_capacity[kCapDevices][kCapTiles][3];
 
-static hipError_t fused_capacity(int dev, int tile, bool out_i32, MmKernel fn, int threads, int &cap)
+static hipError_t fused_capacity(int dev, int tile, int mode, MmKernel fn, int threads, int &cap)
 {
     const bool cached = dev >= 0 && dev < kCapDevices && tile < kCapTiles;
-    if (cached && (cap = g_capacity[dev][tile][out_i32].load(std::memory_order_relaxed)) > 0)
+    if (cached && (cap = g_capacity[dev][tile][mode].load(std::memory_order_relaxed)) > 0)
         return hipSuccess;
     int cus = 0, per_cu = 0;
     hipError_t err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -743,19 +765,19 @@ static hipError_t fused_capacity(int dev, int tile, bool out_i32, MmKernel fn, i
         return err;
     cap = cus * per_cu;
     if (cached && cap > 0)
-        g_capacity[dev][tile][out_i32].store(cap, std::memory_order_relaxed);
+        g_capacity[dev][tile][mode].store(cap, std::memory_order_relaxed);
     return hipSuccess;
 }
 
-hipError_t launch_quant_scaled_mm(MmArgs a, bool out_i32, int tile, hipStream_t stream)
+hipError_t launch_quant_scaled_mm(MmArgs a, int mode, int tile, hipStream_t stream)
 {
     const TileEntry &e = tile_entry(tile);
     const int64_t tiles = ceil_div(a.M, e.bm) * ceil_div(a.N, e.bn);
-    MmKernel fn = out_i32 ? e.i32_fused : e.bf16_fused;
+    MmKernel fn = e.fused[mode];
     if (fn == nullptr)
         return hipErrorNotSupported;
     if (e.skinny)
-        return launch_skinny_quant_mm(a, e, out_i32, stream);
+        return launch_skinny_quant_mm(a, e, mode, stream);
     // Rows per workgroup: enough to cover M with one workgroup per tile,
     // rounded up to a power of two so that it divides BM.
     int rpw = 1;
@@ -774,7 +796,7 @@ hipError_t launch_quant_scaled_mm(MmArgs a, bool out_i32, int tile, hipStream_t 
     // its own-rows fallback keeps an ordinary launch correct even where the
     // grid does not all run at once.)
     int cap = 0;
-    err = fused_capacity(dev, tile, out_i32, fn, e.threads, cap);
+    err = fused_capacity(dev, tile, mode, fn, e.threads, cap);
     if (err != hipSuccess)
         return err;
     if (tiles > cap)

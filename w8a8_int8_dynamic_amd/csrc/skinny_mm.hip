@@ -49,6 +49,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // Fused quant: every workgroup converts its tile's rows itself, about ten
 // VALU operations per element, which only pays below a few rows: tiles of
@@ -73,7 +74,7 @@ struct Skinny {
 // rows are read once: thread t holds chunk c of row r (elements
 // (c*THREADS + t)*8 ..+8) in slot r*cpr + c, at most kQuantSlots of them.
 // Every thread calls this (it holds barriers).
-template <int THREADS>
+template <int THREADS, int E>
 __device__ __forceinline__ void quantize_tile(const MmArgs &a, int m0, int rows, int pitch,
                                               bool writer, int8_t *tok, quant_rule::u32 *rowmax,
                                               float *rowscale)
@@ -98,7 +99,7 @@ __device__ __forceinline__ void quantize_tile(const MmArgs &a, int m0, int rows,
 #pragma unroll
     for (int s = 0; s < kQuantSlots; ++s) {
         if (s < slots) {
-            const u32 m = wave_max(chunk_absmax<false>(v[s]));
+            const u32 m = wave_max(chunk_absmax<E>(v[s]));
             if (lane == 0)
                 atomicMax(&rowmax[s / cpr], m);
         }
@@ -109,10 +110,10 @@ __device__ __forceinline__ void quantize_tile(const MmArgs &a, int m0, int rows,
         if (s < slots) {
             const int r = s / cpr, e = ((s - r * cpr) * THREADS + (int)threadIdx.x) * 8;
             float sc, inv;
-            scale_of(rowmax[r], false, sc, inv);
+            scale_of(rowmax[r], E, sc, inv);
             if (e < a.K) {
                 u32 lo, hi;
-                chunk_codes<false>(v[s], inv, lo, hi);
+                chunk_codes<E>(v[s], inv, lo, hi);
                 *reinterpret_cast<v2u *>(tok + r * pitch + e) = v2u{lo, hi};
                 if (writer)
                     *reinterpret_cast<v2u *>(const_cast<int8_t *>(a.xq) + (int64_t)(m0 + r) * a.ldq + e) =
@@ -122,7 +123,7 @@ __device__ __forceinline__ void quantize_tile(const MmArgs &a, int m0, int rows,
     }
     if ((int)threadIdx.x < rows) {
         float sc, inv;
-        scale_of(rowmax[threadIdx.x], false, sc, inv);
+        scale_of(rowmax[threadIdx.x], E, sc, inv);
         rowscale[threadIdx.x] = sc;
         if (writer)
             const_cast<float *>(a.xs)[m0 + threadIdx.x] = sc;
@@ -132,9 +133,12 @@ __device__ __forceinline__ void quantize_tile(const MmArgs &a, int m0, int rows,
 
 // At least 16 wavefronts per CU (128 registers each): the kernel lives on
 // the loads it keeps in flight, so occupancy counts more than ILP.
-template <class S, bool OUT_I32, bool FUSED>
+template <class S, int OUT, bool FUSED>
 __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kernel(const MmArgs a)
 {
+    constexpr bool OUT_I32 = OUT == kOutI32, OUT_F16 = OUT == kOutF16;
+    // The fused form reads x in the output's 16-bit type (bf16 for int32).
+    constexpr int IN = OUT_F16 ? kElemF16 : kElemBF16;
     // Waves 1 .. WK-1 hand their partial sums to wave 0.
     __shared__ v4i part[S::WK - 1][S::FM * S::FN][64];
     // Fused quant: the tile's codes (rows of K + 16 bytes, sized at launch),
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
 #pragma unroll
         for (int u = 0; u < S::U; ++u)
             wload(min(kb_of(u), KB - 1), w[u]);
-        quantize_tile<S::THREADS>(a, m0, rows, pitch, nb0 == 0, tok, rowmax, rowscale);
+        quantize_tile<S::THREADS, IN>(a, m0, rows, pitch, nb0 == 0, tok, rowmax, rowscale);
         if (pre) {
             v4i x[S::U][S::FM];
 #pragma unroll
@@ -313,12 +317,21 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
                 const int nr = min(n + r, a.N - 1);
                 v[r] = (float)c[r] * xr;
                 v[r] = v[r] * a.ws[nr];
-                if (has_bias)
-                    v[r] = v[r] + __uint_as_float((unsigned)a.bias[nr] << 16);
+                if (has_bias) {
+                    const unsigned b = a.bias[nr];
+                    v[r] = v[r] + (OUT_F16 ? quant_rule::f16_to_float(b) : __uint_as_float(b << 16));
+                }
             }
-            const bf16x2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, bf16x2);
-            const bf16x2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, bf16x2);
-            const v2u pk = v2u{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+            v2u pk;
+            if (OUT_F16) {
+                const f16x2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, f16x2);
+                const f16x2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, f16x2);
+                pk = v2u{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+            } else {
+                const bf16x2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, bf16x2);
+                const bf16x2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, bf16x2);
+                pk = v2u{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+            }
             uint16_t *o = reinterpret_cast<uint16_t *>(a.out) + (int64_t)m * a.ldo + n;
             if (whole) {
                 *reinterpret_cast<v2u *>(o) = pk;
@@ -336,9 +349,11 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
 template <class S>
 constexpr TileEntry skinny(const char *name)
 {
-    return TileEntry{name, S::BM, S::BN, S::THREADS, true, skinny_mm_kernel<S, false, false>,
-                     skinny_mm_kernel<S, true, false>, skinny_mm_kernel<S, false, true>,
-                     skinny_mm_kernel<S, true, true>};
+    return TileEntry{name, S::BM, S::BN, S::THREADS, true,
+                     {skinny_mm_kernel<S, kOutBF16, false>, skinny_mm_kernel<S, kOutI32, false>,
+                      skinny_mm_kernel<S, kOutF16, false>},
+                     {skinny_mm_kernel<S, kOutBF16, true>, skinny_mm_kernel<S, kOutI32, true>,
+                      skinny_mm_kernel<S, kOutF16, true>}};
 }
 
 // 16*FM token rows x 16*FN channels / WK waves along K / U k-blocks per
@@ -355,7 +370,7 @@ const TileEntry kSkinny[] = {
 int skinny_tile_count() { return (int)(sizeof(kSkinny) / sizeof(kSkinny[0])); }
 const TileEntry &skinny_tile(int i) { return kSkinny[i]; }
 
-hipError_t launch_skinny_quant_mm(const MmArgs &a, const TileEntry &e, bool out_i32,
+hipError_t launch_skinny_quant_mm(const MmArgs &a, const TileEntry &e, int mode,
                                   hipStream_t stream)
 {
     const int64_t rows = std::min<int64_t>(a.M, e.bm);
@@ -364,7 +379,7 @@ hipError_t launch_skinny_quant_mm(const MmArgs &a, const TileEntry &e, bool out_
         return hipErrorNotSupported;
     const size_t lds = (size_t)(rows * (a.K + 16));
     const int64_t tiles = ceil_div(a.M, e.bm) * ceil_div(a.N, e.bn);
-    hipLaunchKernelGGL(out_i32 ? e.i32_fused : e.bf16_fused, dim3((unsigned)tiles), dim3(e.threads),
+    hipLaunchKernelGGL(e.fused[mode], dim3((unsigned)tiles), dim3(e.threads),
                        lds, stream, a);
     return hipGetLastError();
 }

@@ -18,7 +18,7 @@ __all__ = ["W8A8Linear"]
 
 
 class W8A8Linear(torch.nn.Module):
-    """y = bf16( int8(x) @ int8(W)^T * x_scale * w_scale (+ bias) ).
+    """y = int8(x) @ int8(W)^T * x_scale * w_scale (+ bias), in x's type (bf16 or fp16).
 
     Build with ``from_float`` (online per-channel weight quantization on the
     GPU, written straight into the load-time layout) or ``from_quantized``
@@ -32,7 +32,9 @@ class W8A8Linear(torch.nn.Module):
         self.out_features = out_features
         self.register_buffer("w_packed", w_packed)
         self.register_buffer("w_scale", w_scale)
-        self.register_buffer("bias", bias)
+        # The bias in each output type, rounded once from what was given.
+        self.register_buffer("bias", None if bias is None else bias.to(torch.bfloat16).contiguous())
+        self.register_buffer("bias_f16", None if bias is None else bias.to(torch.float16).contiguous())
 
     @classmethod
     def from_quantized(cls, wq: torch.Tensor, w_scale: torch.Tensor,
@@ -41,8 +43,7 @@ class W8A8Linear(torch.nn.Module):
         if not torch.isfinite(w_scale).all():
             raise ValueError("weight scales must be finite")
         packed = ops.prepack_weight(wq.contiguous())
-        b = None if bias is None else bias.to(torch.bfloat16).contiguous()
-        return cls(packed, w_scale.to(torch.float32).contiguous(), N, K, b)
+        return cls(packed, w_scale.to(torch.float32).contiguous(), N, K, bias)
 
     @classmethod
     def from_float(cls, weight: torch.Tensor, bias: Optional[torch.Tensor] = None) -> "W8A8Linear":
@@ -53,8 +54,7 @@ class W8A8Linear(torch.nn.Module):
         packed, ws = ops.quant_prepack_weight(w.contiguous())
         if not torch.isfinite(ws).all():
             raise ValueError("weight scales must be finite")
-        b = None if bias is None else bias.to(torch.bfloat16).contiguous()
-        return cls(packed, ws, N, K, b)
+        return cls(packed, ws, N, K, bias)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         if x.shape[-1] != self.in_features:
@@ -63,9 +63,10 @@ class W8A8Linear(torch.nn.Module):
         x2 = x.reshape(-1, self.in_features)
         if x2.stride(-1) != 1:
             x2 = x2.contiguous()
-        # The per-token quant and the scaled matmul, as one library call.
-        out, _, _ = ops.quant_scaled_mm(x2, self.w_packed, self.w_scale, self.out_features,
-                                        self.bias)
+        # The per-token quant and the scaled matmul, as one library call; the
+        # output (and bias) type is x's.
+        bias = self.bias_f16 if x2.dtype == torch.float16 else self.bias
+        out, _, _ = ops.quant_scaled_mm(x2, self.w_packed, self.w_scale, self.out_features, bias)
         return out.reshape(*lead, self.out_features)
 
     def extra_repr(self) -> str:

@@ -13,7 +13,7 @@ from typing import Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import W8A8_OUT_BF16, W8A8_OUT_I32, call
+from ._lib import W8A8_OUT_BF16, W8A8_OUT_F16, W8A8_OUT_I32, call
 
 __all__ = ["quant_per_token", "quant_per_channel", "prepack_weight", "quant_prepack_weight", "unpack_weight",
            "prepack_weight_bytes", "scaled_mm", "quant_scaled_mm", "tile_count", "tile_name",
@@ -69,10 +69,26 @@ def _codes(M: int, K: int, device) -> torch.Tensor:
     return torch.empty((M, _round_up(K, 16)), dtype=torch.int8, device=device)[:, :K]
 
 
+_ACT_ENTRY = {torch.bfloat16: "", torch.float16: "_f16"}
+_OUT_MODE = {torch.bfloat16: W8A8_OUT_BF16, torch.float16: W8A8_OUT_F16, torch.int32: W8A8_OUT_I32}
+
+
+def _act_dtype(x: torch.Tensor) -> torch.dtype:
+    if x.dtype not in _ACT_ENTRY:
+        raise TypeError(f"x must be bfloat16 or float16, got {x.dtype}")
+    return x.dtype
+
+
+def _out_mode(out_dtype: torch.dtype) -> int:
+    if out_dtype not in _OUT_MODE:
+        raise TypeError("out_dtype must be torch.bfloat16, torch.float16 or torch.int32")
+    return _OUT_MODE[out_dtype]
+
+
 def quant_per_token(x: torch.Tensor, xq: Optional[torch.Tensor] = None,
                     xs: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Per-token dynamic quantization of bf16 x [M, K] -> (int8 [M, K], fp32 [M])."""
-    _matrix(x, "x", torch.bfloat16)
+    """Per-token dynamic quantization of bf16 or fp16 x [M, K] -> (int8 [M, K], fp32 [M])."""
+    _matrix(x, "x", _act_dtype(x))
     M, K = x.shape
     x = _rows_aligned(x, 8)
     if xq is None:
@@ -82,8 +98,8 @@ def quant_per_token(x: torch.Tensor, xq: Optional[torch.Tensor] = None,
     _matrix(xq, "xq", torch.int8)
     _vector(xs, M, "xs", torch.float32)
     with torch.cuda.device(x.device):
-        call("int8_quant_per_token", x.data_ptr(), M, K, _ld(x), xq.data_ptr(), _ld(xq),
-             xs.data_ptr(), _stream(x))
+        call("int8_quant_per_token" + _ACT_ENTRY[x.dtype], x.data_ptr(), M, K, _ld(x),
+             xq.data_ptr(), _ld(xq), xs.data_ptr(), _stream(x))
     return xq, xs
 
 
@@ -149,18 +165,15 @@ def scaled_mm(xq: torch.Tensor, xs: Optional[torch.Tensor], w_packed: torch.Tens
               ws: Optional[torch.Tensor], N: int, bias: Optional[torch.Tensor] = None,
               out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
               tile: int = -1) -> torch.Tensor:
-    """out[m, n] = bf16(acc * xs[m] * ws[n] (+ bias[n])), or int32 acc when out_dtype=int32."""
+    """out[m, n] = acc * xs[m] * ws[n] (+ bias[n]) rounded to out_dtype (bf16 or fp16;
+    the bias in the same type), or the int32 accumulators when out_dtype=int32."""
     _matrix(xq, "xq", torch.int8)
     M, K = xq.shape
-    if out_dtype == torch.bfloat16:
-        mode = W8A8_OUT_BF16
+    mode = _out_mode(out_dtype)
+    if mode != W8A8_OUT_I32:
         _vector(xs, M, "xs", torch.float32)
         _vector(ws, N, "ws", torch.float32)
-        _vector(bias, N, "bias", torch.bfloat16)
-    elif out_dtype == torch.int32:
-        mode = W8A8_OUT_I32
-    else:
-        raise TypeError("out_dtype must be torch.bfloat16 or torch.int32")
+        _vector(bias, N, "bias", out_dtype)
     if not w_packed.is_cuda or w_packed.dtype != torch.uint8 or \
             w_packed.numel() < prepack_weight_bytes(N, K):
         raise ValueError("w_packed must be a uint8 device buffer from prepack_weight(N, K)")
@@ -180,25 +193,24 @@ def scaled_mm(xq: torch.Tensor, xs: Optional[torch.Tensor], w_packed: torch.Tens
 
 
 def quant_scaled_mm(x: torch.Tensor, w_packed: torch.Tensor, ws: Optional[torch.Tensor], N: int,
-                    bias: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+                    bias: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
                     out: Optional[torch.Tensor] = None, tile: int = -1,
                     xq: Optional[torch.Tensor] = None, xs: Optional[torch.Tensor] = None
                     ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Per-token quant of bf16 x [M, K] and the scaled matmul in one call.
+    """Per-token quant of bf16 or fp16 x [M, K] and the scaled matmul in one call.
 
-    Returns (out, xq, xs): out as scaled_mm returns it, and the int8 codes and
-    fp32 scales the quant produced (bit-identical to quant_per_token)."""
-    _matrix(x, "x", torch.bfloat16)
+    out_dtype defaults to x's type. Returns (out, xq, xs): out as scaled_mm
+    returns it, and the int8 codes and fp32 scales the quant produced
+    (bit-identical to quant_per_token)."""
+    _matrix(x, "x", _act_dtype(x))
+    if out_dtype is None:
+        out_dtype = x.dtype
     M, K = x.shape
     x = _rows_aligned(x, 8)
-    if out_dtype == torch.bfloat16:
-        mode = W8A8_OUT_BF16
+    mode = _out_mode(out_dtype)
+    if mode != W8A8_OUT_I32:
         _vector(ws, N, "ws", torch.float32)
-        _vector(bias, N, "bias", torch.bfloat16)
-    elif out_dtype == torch.int32:
-        mode = W8A8_OUT_I32
-    else:
-        raise TypeError("out_dtype must be torch.bfloat16 or torch.int32")
+        _vector(bias, N, "bias", out_dtype)
     if not w_packed.is_cuda or w_packed.dtype != torch.uint8 or \
             w_packed.numel() < prepack_weight_bytes(N, K):
         raise ValueError("w_packed must be a uint8 device buffer from prepack_weight(N, K)")
@@ -220,9 +232,9 @@ def quant_scaled_mm(x: torch.Tensor, w_packed: torch.Tensor, ws: Optional[torch.
         return None if t is None or mode == W8A8_OUT_I32 else t.data_ptr()
 
     with torch.cuda.device(x.device):
-        call("int8_quant_scaled_mm_tile", x.data_ptr(), _ld(x), xq.data_ptr(), _ld(xq),
-             xs.data_ptr(), w_packed.data_ptr(), ptr(ws), ptr(bias), M, N, K, mode,
-             out.data_ptr(), _ld(out), _stream(x), tile)
+        call("int8_quant_scaled_mm" + _ACT_ENTRY[x.dtype] + "_tile", x.data_ptr(), _ld(x),
+             xq.data_ptr(), _ld(xq), xs.data_ptr(), w_packed.data_ptr(), ptr(ws), ptr(bias), M,
+             N, K, mode, out.data_ptr(), _ld(out), _stream(x), tile)
     return out, xq, xs
 
 
