@@ -58,6 +58,10 @@ class Oracle:
             "oracle_quant_rows_f16": [vp, i64, i64, i64, vp, i64, vp],
             "oracle_epilogue_f32_f16": [vp, i64, i64, i64, vp, vp, vp, vp, i64],
             "oracle_epilogue_f64_f16": [vp, i64, i64, i64, vp, vp, vp, vp, i64],
+            "oracle_fp8_quant_rows_bf16": [vp, i64, i64, i64, vp, i64, vp],
+            "oracle_fp8_quant_rows_f32": [vp, i64, i64, i64, vp, i64, vp],
+            "oracle_fp8_gemm_rows": [vp, i64, vp, i64, vp, i64, i64, i64, vp, i64],
+            "oracle_fp8_epilogue": [vp, i64, i64, i64, vp, vp, vp, vp, vp, i64],
         }.items():
             fn = getattr(lib, name)
             fn.argtypes = args
@@ -70,6 +74,10 @@ class Oracle:
         lib.oracle_double_to_f16.restype = ctypes.c_uint16
         lib.oracle_f16_to_float.argtypes = [ctypes.c_uint16]
         lib.oracle_f16_to_float.restype = ctypes.c_float
+        lib.oracle_double_to_e4m3.argtypes = [ctypes.c_double]
+        lib.oracle_double_to_e4m3.restype = ctypes.c_uint8
+        lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_to_double.restype = ctypes.c_double
         self.lib = lib
 
     @staticmethod
@@ -169,6 +177,63 @@ class Oracle:
 
     def double_to_bf16(self, d: float) -> int:
         return int(self.lib.oracle_double_to_bf16(d))
+
+    # -- the FP8 (e4m3) twin -------------------------------------------------
+    def fp8_quant_per_token(self, x_bf16: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+        x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+        M, K = x.shape
+        q = np.empty((M, K), dtype=np.uint8)
+        s = np.empty(M, dtype=np.float32)
+        self._check(self.lib.oracle_fp8_quant_rows_bf16(_p(x), M, K, K, _p(q), K, _p(s)),
+                    "fp8_quant_per_token")
+        return q, s
+
+    def fp8_quant_per_channel(self, w_f32: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+        w = np.ascontiguousarray(w_f32, dtype=np.float32)
+        N, K = w.shape
+        q = np.empty((N, K), dtype=np.uint8)
+        s = np.empty(N, dtype=np.float32)
+        self._check(self.lib.oracle_fp8_quant_rows_f32(_p(w), N, K, K, _p(q), K, _p(s)),
+                    "fp8_quant_per_channel")
+        return q, s
+
+    def fp8_gemm(self, xq: np.ndarray, wq: np.ndarray,
+                 rows: Optional[np.ndarray] = None) -> np.ndarray:
+        """Exact (float64) sums of products of the decoded e4m3 codes."""
+        a = np.ascontiguousarray(xq, dtype=np.uint8)
+        b = np.ascontiguousarray(wq, dtype=np.uint8)
+        M, K = a.shape
+        N, K2 = b.shape
+        if K != K2:
+            raise ValueError("inner dimensions differ")
+        r = None
+        if rows is not None:
+            r = np.ascontiguousarray(rows, dtype=np.int64)
+            M = r.size
+        acc = np.empty((M, N), dtype=np.float64)
+        self._check(self.lib.oracle_fp8_gemm_rows(_p(a), K, _p(r), M, _p(b), K, N, K, _p(acc), N),
+                    "fp8_gemm")
+        return acc
+
+    def fp8_epilogue(self, acc, xs, ws, bias=None) -> Tuple[np.ndarray, np.ndarray]:
+        """(bf16 bits of the fp32-order epilogue on fl32(acc), bf16 bits of the
+        fp64 value rounded once)."""
+        acc = np.ascontiguousarray(acc, dtype=np.float64)
+        xs = np.ascontiguousarray(xs, dtype=np.float32)
+        ws = np.ascontiguousarray(ws, dtype=np.float32)
+        b = None if bias is None else np.ascontiguousarray(bias, dtype=np.uint16)
+        M, N = acc.shape
+        o32 = np.empty((M, N), dtype=np.uint16)
+        o64 = np.empty((M, N), dtype=np.uint16)
+        self._check(self.lib.oracle_fp8_epilogue(_p(acc), N, M, N, _p(xs), _p(ws), _p(b), _p(o32),
+                                                 _p(o64), N), "fp8_epilogue")
+        return o32, o64
+
+    def double_to_e4m3(self, d: float) -> int:
+        return int(self.lib.oracle_double_to_e4m3(d))
+
+    def e4m3_to_double(self, c: int) -> float:
+        return float(self.lib.oracle_e4m3_to_double(c))
 
     # -- the whole layer ----------------------------------------------------
     def linear(self, x_bf16, wq, ws, bias=None, rows=None, f64=False):

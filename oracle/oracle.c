@@ -348,6 +348,178 @@ int oracle_epilogue_f64_f16(const int32_t *acc, int64_t ldc, int64_t M, int64_t 
     return ORACLE_OK;
 }
 
+/* ---------------------------------------------------------------------
+ * The FP8 (e4m3) W8A8 twin (page "Online Quantization": FP8 W8A8 with the
+ * "dynamic" activation scheme in its Parameters table). The pages give no
+ * formula; the reading mirrors the int8 path: per-token activation scales
+ * and per-output-channel weight scales, scale = absmax / 448 (448 is the
+ * largest finite OCP e4m3 value), code = e4m3_rne(clamp(x * fl32(448 /
+ * absmax), -448, 448)), a row below 2^-100 gets scale 0 and zero codes.
+ * Products of two e4m3 values and their sums over K are exact in double
+ * (every product is a multiple of 2^-18 below 2^18), so the accumulators
+ * here are exact; the epilogue takes them rounded once to fp32.
+ * OCP e4m3: sign, 4 exponent bits (bias 7), 3 mantissa bits; no infinity;
+ * S.1111.111 is NaN; subnormals m * 2^-9.
+ * --------------------------------------------------------------------- */
+static double e4m3_to_double(uint8_t c)
+{
+    int sign = c >> 7, e = (c >> 3) & 0xf, m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp((double)(8 + m), e - 10);
+    return sign ? -v : v;
+}
+
+/* Round to e4m3 once, nearest-even; |d| must not exceed 448 (callers
+ * clamp first), so no result leaves the finite range. */
+static uint8_t double_to_e4m3_rne(double d)
+{
+    uint8_t sign = signbit(d) ? 0x80u : 0x00u;
+    double a = fabs(d);
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);                                   /* a in [2^(e-1), 2^e) */
+    int q = e - 4;                                  /* step of a 4-bit significand */
+    if (q < -9)
+        q = -9;                                     /* subnormal step 2^-9 */
+    double r = nearbyint(ldexp(a, -q));             /* ties to even */
+    if (r == 0.0)
+        return sign;
+    int k;
+    frexp(r, &k);
+    int exp_unbiased = q + k - 1;
+    if (exp_unbiased < -6)                          /* subnormal: bits are r */
+        return sign | (uint8_t)r;
+    uint32_t sig = (uint32_t)ldexp(r, 4 - k);       /* 4 bits, leading one at bit 3 */
+    return sign | (uint8_t)((exp_unbiased + 7) << 3) | (uint8_t)(sig & 7u);
+}
+
+static void quantize_row_fp8(const float *v, int64_t K, uint8_t *q, float *scale)
+{
+    float a = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        float m = fabsf(v[k]);
+        if (m > a)
+            a = m;
+    }
+    if (a < 0x1p-100f) {
+        *scale = 0.0f;
+        for (int64_t k = 0; k < K; ++k)
+            q[k] = 0;
+        return;
+    }
+    float s = a / 448.0f;
+    float inv = 448.0f / a;
+    for (int64_t k = 0; k < K; ++k) {
+        float t = v[k] * inv;
+        if (t > 448.0f)
+            t = 448.0f;
+        if (t < -448.0f)
+            t = -448.0f;
+        q[k] = double_to_e4m3_rne((double)t);
+    }
+    *scale = s;
+}
+
+/* FP8 codes of bf16 rows (activations, per token) or fp32 rows (weights,
+ * per output channel). */
+int oracle_fp8_quant_rows_bf16(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                               uint8_t *q, int64_t ldq, float *scale)
+{
+    if (M < 0 || K < 1 || ldx < K || ldq < K || (M > 0 && (!x || !q || !scale)))
+        return ORACLE_ERR_ARGS;
+    int failed = 0;
+#pragma omp parallel reduction(| : failed)
+    {
+        float *row = (float *)malloc((size_t)K * sizeof(float));
+        if (!row) {
+            failed = 1;
+        } else {
+            int64_t m;
+#pragma omp for schedule(static)
+            for (m = 0; m < M; ++m) {
+                for (int64_t k = 0; k < K; ++k)
+                    row[k] = bf16_bits_to_float(x[m * ldx + k]);
+                quantize_row_fp8(row, K, q + m * ldq, &scale[m]);
+            }
+            free(row);
+        }
+    }
+    return failed ? ORACLE_ERR_ARGS : ORACLE_OK;
+}
+
+int oracle_fp8_quant_rows_f32(const float *w, int64_t N, int64_t K, int64_t ldw, uint8_t *q,
+                              int64_t ldq, float *scale)
+{
+    if (N < 0 || K < 1 || ldw < K || ldq < K || (N > 0 && (!w || !q || !scale)))
+        return ORACLE_ERR_ARGS;
+    int64_t n;
+#pragma omp parallel for schedule(static)
+    for (n = 0; n < N; ++n)
+        quantize_row_fp8(w + n * ldw, K, q + n * ldq, &scale[n]);
+    return ORACLE_OK;
+}
+
+/* acc[i, n] = sum_k dec(A[rows[i], k]) * dec(B[n, k]), exact (double). */
+int oracle_fp8_gemm_rows(const uint8_t *a, int64_t lda, const int64_t *rows, int64_t M,
+                         const uint8_t *b, int64_t ldb, int64_t N, int64_t K, double *acc,
+                         int64_t ldc)
+{
+    if (M < 0 || N < 1 || K < 1 || lda < K || ldb < K || ldc < N ||
+        (M > 0 && (!a || !b || !acc)))
+        return ORACLE_ERR_ARGS;
+    int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < M; ++i) {
+        const uint8_t *ar = a + (rows ? rows[i] : i) * lda;
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t *br = b + n * ldb;
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                s += e4m3_to_double(ar[k]) * e4m3_to_double(br[k]);
+            acc[i * ldc + n] = s;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* The epilogue on exact accumulators: fl32(acc), then the fp32 order of
+ * oracle_epilogue_f32 (bf16 bias and output); and the fp64 value rounded
+ * once, the tolerance reference. */
+int oracle_fp8_epilogue(const double *acc, int64_t ldc, int64_t M, int64_t N, const float *xs,
+                        const float *ws, const uint16_t *bias, uint16_t *out32, uint16_t *out64,
+                        int64_t ldo)
+{
+    if (M < 0 || N < 1 || ldc < N || ldo < N ||
+        (M > 0 && (!acc || !xs || !ws || !out32 || !out64)))
+        return ORACLE_ERR_ARGS;
+    int64_t m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            float t = (float)acc[m * ldc + n];
+            t = t * xs[m];
+            t = t * ws[n];
+            if (bias)
+                t = t + bf16_bits_to_float(bias[n]);
+            out32[m * ldo + n] = float_to_bf16_rne(t);
+            double d = acc[m * ldc + n] * (double)xs[m] * (double)ws[n];
+            if (bias)
+                d += (double)bf16_bits_to_float(bias[n]);
+            out64[m * ldo + n] = double_to_bf16_rne(d);
+        }
+    }
+    return ORACLE_OK;
+}
+
+uint8_t oracle_double_to_e4m3(double d) { return double_to_e4m3_rne(d); }
+double oracle_e4m3_to_double(uint8_t c) { return e4m3_to_double(c); }
+
 /* Exposed for the pins: the scalar conversions used above. */
 uint16_t oracle_float_to_bf16(float f) { return float_to_bf16_rne(f); }
 uint16_t oracle_double_to_bf16(double d) { return double_to_bf16_rne(d); }

@@ -368,6 +368,119 @@ def pin_epilogue_f16_exact(o):
 
 
 # ---------------------------------------------------------------------------
+# The FP8 (e4m3) twin
+# ---------------------------------------------------------------------------
+def _exact_e4m3(v: Fraction) -> int:
+    """OCP e4m3 bits of the exact rational v (|v| <= 448), nearest-even."""
+    neg = v < 0
+    v = -v if neg else v
+    sign = 0x80 if neg else 0
+    if v == 0:
+        return sign
+    e = v.numerator.bit_length() - v.denominator.bit_length()
+    if Fraction(2) ** e > v:
+        e -= 1
+    ulp = Fraction(2) ** (max(e, -6) - 3)          # 4 significant bits, or subnormal step 2^-9
+    t = v / ulp
+    r = int(t)
+    frac = t - r
+    if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and r % 2 == 1):
+        r += 1
+    val = r * ulp
+    assert val <= 448
+    if val < Fraction(2) ** -6:
+        return sign | int(val / Fraction(2) ** -9)
+    E = val.numerator.bit_length() - val.denominator.bit_length()
+    if Fraction(2) ** E > val:
+        E -= 1
+    mant = int(val / Fraction(2) ** E * 8) - 8
+    return sign | ((E + 7) << 3) | mant
+
+
+def pin_e4m3_conversions(o):
+    import torch
+    for c in range(256):
+        ref = torch.tensor([c], dtype=torch.uint8).view(torch.float8_e4m3fn).double().item()
+        got = o.e4m3_to_double(c)
+        assert got == ref or (np.isnan(got) and np.isnan(ref)), c
+    for d, bits in [(448.0, 0x7E), (-448.0, 0xFE), (2.0 ** -9, 0x01), (2.0 ** -10, 0x00),
+                    (3 * 2.0 ** -10, 0x02), (1.0 + 2.0 ** -4, 0x38), (1.0 + 3 * 2.0 ** -4, 0x3A),
+                    (1.0 + 2.0 ** -4 + 2.0 ** -30, 0x39), (2.0 ** -6 - 2.0 ** -10, 0x08),
+                    (-0.0, 0x80), (240.0, 0x77)]:
+        assert o.double_to_e4m3(d) == bits, (d, hex(o.double_to_e4m3(d)))
+    rng = np.random.default_rng(31)
+    v = np.clip(rng.standard_normal(3000) * 10.0 ** rng.uniform(-4, 2.7, 3000), -448, 448)
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for x, r in zip(v.astype(np.float32), ref):
+        got = o.double_to_e4m3(float(x))
+        assert got == int(r) == _exact_e4m3(Fraction(float(x))), x
+
+
+def pin_fp8_quant(o):
+    rng = np.random.default_rng(32)
+    x = (rng.standard_normal((24, 300)) * 10.0 ** rng.uniform(-3, 3, (24, 1))).astype(np.float32)
+    x[2] = 0.0
+    x[4, 9] = -np.abs(x[4]).max() * 2                  # negative argmax
+    xb = wl.f32_to_bf16_bits(x)
+    q, s = o.fp8_quant_per_token(xb)
+    xf = _bf16_to_f64(xb)
+    dec = np.vectorize(o.e4m3_to_double)(q)
+    assert s[2] == 0 and not q[2].any()
+    assert not np.any((q & 0x7F) == 0x7F)               # never NaN
+    am = np.argmax(np.abs(xf), axis=1)
+    live = s > 0
+    assert np.all(np.abs(dec[np.arange(24), am])[live] == 448.0)
+    # each code is the nearest e4m3 value of x / s: within half a step
+    # (relative 2^-4, absolute 2^-10 in the subnormal range), plus fp32 slack
+    y = xf / np.where(live, s, 1).astype(np.float64)[:, None]
+    err = np.abs(dec - y)
+    assert np.all(err[live] <= (np.abs(y) * 2.0 ** -4 + 2.0 ** -10 + np.abs(y) * 2.0 ** -20)[live])
+    # odd symmetry (signed zeros included: negating x flips every code's
+    # sign bit) and the weight path on the same rows
+    qn, sn = o.fp8_quant_per_token(wl.f32_to_bf16_bits(-x))
+    assert np.array_equal(sn, s) and np.array_equal(qn[live], q[live] ^ 0x80)
+    qw, sw = o.fp8_quant_per_channel(_f32(xb))
+    assert np.array_equal(qw, q) and np.array_equal(sw, s)
+
+
+def pin_fp8_gemm(o):
+    rng = np.random.default_rng(33)
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    a = rng.choice(codes, (5, 37))
+    b = rng.choice(codes, (6, 37))
+    acc = o.fp8_gemm(a, b)
+    frac = {int(c): Fraction(o.e4m3_to_double(int(c))) for c in codes}
+    for i in range(5):
+        for n in range(6):
+            assert Fraction(acc[i, n]) == sum(frac[int(a[i, k])] * frac[int(b[n, k])] for k in range(37))
+    a = rng.choice(codes, (64, 4096))
+    b = rng.choice(codes, (48, 4096))
+    dec = np.vectorize(o.e4m3_to_double)
+    assert np.array_equal(o.fp8_gemm(a, b), dec(a) @ dec(b).T)     # exact sums either way
+    rows = np.array([5, 0, 63])
+    assert np.array_equal(o.fp8_gemm(a, b, rows), (dec(a) @ dec(b).T)[rows])
+
+
+def pin_fp8_epilogue(o):
+    rng = np.random.default_rng(34)
+    M, N = 5, 6
+    acc = (rng.standard_normal((M, N)) * 1e4).round(3)
+    xs = rng.uniform(0.01, 1, M).astype(np.float32)
+    ws = rng.uniform(1e-4, 1e-2, N).astype(np.float32)
+    bias = wl.f32_to_bf16_bits(rng.standard_normal(N).astype(np.float32) * np.float32(0.01))
+    for b in (None, bias):
+        o32, o64 = o.fp8_epilogue(acc, xs, ws, b)
+        for m in range(M):
+            for n in range(N):
+                v = Fraction(float(acc[m, n])) * Fraction(float(xs[m])) * Fraction(float(ws[n]))
+                if b is not None:
+                    v += Fraction(float(_f32(b[n:n + 1])[0]))
+                assert o64[m, n] == _exact_bf16(v), (m, n)
+                t = np.float32(acc[m, n]) * xs[m] * ws[n]
+                assert abs(int(o32[m, n]) - int(o64[m, n])) <= 1 or np.sign(t) == 0
+
+
+# ---------------------------------------------------------------------------
 # Whole layer
 # ---------------------------------------------------------------------------
 def _dequant_reference(xq, xs, wq, ws, bias=None):
@@ -485,6 +598,7 @@ def pin_pages_missing_act_scale(o, rows: int = 64):
 
 FAST_PINS = [pin_quant_ties, pin_quant_zero_rows, pin_quant_invariants, pin_gemm_bruteforce,
              pin_gemm_numpy, pin_bf16_rounding, pin_epilogue_exact, pin_f16_conversions,
-             pin_quant_f16, pin_epilogue_f16_exact, pin_layer_vs_numpy, pin_fused_qkv_stack]
+             pin_quant_f16, pin_epilogue_f16_exact, pin_e4m3_conversions, pin_fp8_quant,
+             pin_fp8_gemm, pin_fp8_epilogue, pin_layer_vs_numpy, pin_fused_qkv_stack]
 PAGE_PINS = [pin_pages_rel_l2, pin_pages_missing_act_scale]
 ALL_PINS = FAST_PINS + PAGE_PINS

@@ -31,7 +31,8 @@ MUTANTS = {
     "bf16_round_half_up": ("u += 0x7fffu + lsb;", "u += 0x8000u + 0u * lsb;"),
     "xs_indexed_by_column": ("t = t * xs[m];", "t = t * xs[n % M];"),
     "f64_double_rounding": ("double r = nearbyint(ldexp(m, 8));", "double r = nearbyint(ldexp((float)m, 8));"),
-    "f16_truncate": ("double r = nearbyint(ldexp(a, -q));", "double r = floor(ldexp(a, -q));"),
+    "f16_truncate": ("double r = nearbyint(ldexp(a, -q));             /* a / 2^q, ties to even */",
+                     "double r = floor(ldexp(a, -q));"),
     "f16_coarse_subnormals": ("q = -24;                                    /* subnormal step 2^-24 */",
                               "q = -23;"),
     "f16_overflow_early": ("if (a >= 65520.0)", "if (a > 65504.0)"),
@@ -39,6 +40,17 @@ MUTANTS = {
     "f16_bias_dropped": ("t = t + f16_bits_to_float(bias[n]);", "t = t;"),
     "f16_out_through_bf16": ("out[m * ldo + n] = double_to_f16_rne((double)t);",
                              "out[m * ldo + n] = double_to_f16_rne((double)bf16_bits_to_float(float_to_bf16_rne(t)));"),
+    "fp8_max_240": ("float s = a / 448.0f;", "float s = a / 240.0f;"),
+    "fp8_inv_240": ("float inv = 448.0f / a;", "float inv = 240.0f / a;"),
+    "fp8_truncate": ("double r = nearbyint(ldexp(a, -q));             /* ties to even */",
+                     "double r = floor(ldexp(a, -q));"),
+    "fp8_coarse_subnormals": ("q = -9;                                     /* subnormal step 2^-9 */",
+                              "q = -8;"),
+    "fp8_decode_exponent": ("v = ldexp((double)(8 + m), e - 10);", "v = ldexp((double)(8 + m), e - 9);"),
+    "fp8_gemm_raw_weight": ("s += e4m3_to_double(ar[k]) * e4m3_to_double(br[k]);",
+                            "s += e4m3_to_double(ar[k]) * (double)br[k];"),
+    "fp8_epilogue_drops_xs": ("double d = acc[m * ldc + n] * (double)xs[m] * (double)ws[n];",
+                              "double d = acc[m * ldc + n] * (double)ws[n];"),
 }
 
 
