@@ -261,6 +261,54 @@ w8a8_status_t int8_quant_scaled_mm_tile(const uint16_t *x, int64_t ldx, int8_t *
                                         int64_t N, int64_t K, int mode, void *out, int64_t ldo,
                                         void *stream, int tile);
 
+/*
+ * ---- The FP8 (e4m3) W8A8 twin ----
+ * (Page "Online Quantization": FP8 W8A8 is the sibling method of Int8 W8A8
+ * in its method and hardware tables, with the "dynamic" activation scheme
+ * of its Parameters table.) The pages give no formula for it; this library
+ * reads it the way of the int8 path, with OCP e4m3 codes (largest finite
+ * value 448, the format the gfx950 fp8 MFMA takes):
+ *   per row (token, or output channel) a = max |x|;  a < 2^-100 -> scale 0,
+ *   codes 0; else scale = fl32(a/448), inv = fl32(448/a),
+ *   code = e4m3(clamp(fl32(x*inv), -448, 448)), nearest-even, sign kept
+ *   (zeros too; code 0x80 is -0).
+ *   acc[m,n] = sum_k e4m3(xq[m,k]) * e4m3(wq[n,k]) on the fp8 MFMA with fp32
+ *   accumulation: unlike the int8 path, the sums depend on the hardware's
+ *   summation order (each partial fp32 sum rounded).
+ *   out: the epilogue of int8_scaled_mm on acc (same order and modes;
+ *   W8A8_OUT_I32 stores the raw fp32 accumulators as 4-byte floats).
+ * Codes are uint8 bit patterns. The packed weight uses the layout of
+ * int8_prepack_weight (a byte permutation; int8_prepack_weight packs e4m3
+ * codes as well). Requirements are those of the int8 counterparts.
+ */
+w8a8_status_t fp8_quant_per_token(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                                  uint8_t *xq, int64_t ldq, float *x_scale, void *stream);
+w8a8_status_t fp8_quant_per_channel(const float *w, int64_t N, int64_t K, int64_t ldw,
+                                    uint8_t *wq, int64_t ldq, float *w_scale, void *stream);
+/* Online weight quant from bf16 or fp32 straight into the packed layout, as
+ * int8_quant_prepack_weight with e4m3 codes. */
+w8a8_status_t fp8_quant_prepack_weight(const void *w, int w_dtype, int64_t N, int64_t K,
+                                       int64_t ldw, void *w_packed, float *w_scale,
+                                       void *stream);
+w8a8_status_t fp8_scaled_mm(const uint8_t *xq, int64_t ldq, const float *x_scale,
+                            const void *w_packed, const float *w_scale, const uint16_t *bias,
+                            int64_t M, int64_t N, int64_t K, int mode, void *out, int64_t ldo,
+                            void *stream);
+/* fp8_scaled_mm with an explicit tile (0 <= tile < w8a8_fp8_tile_count(), the
+ * main kernel's configurations, named by w8a8_mm_tile_name) or -1. */
+w8a8_status_t fp8_scaled_mm_tile(const uint8_t *xq, int64_t ldq, const float *x_scale,
+                                 const void *w_packed, const float *w_scale, const uint16_t *bias,
+                                 int64_t M, int64_t N, int64_t K, int mode, void *out, int64_t ldo,
+                                 void *stream, int tile);
+/* fp8_quant_per_token of bf16 x, then fp8_scaled_mm (two launches), writing
+ * xq and x_scale too. */
+w8a8_status_t fp8_quant_scaled_mm(const uint16_t *x, int64_t ldx, uint8_t *xq, int64_t ldq,
+                                  float *x_scale, const void *w_packed, const float *w_scale,
+                                  const uint16_t *bias, int64_t M, int64_t N, int64_t K, int mode,
+                                  void *out, int64_t ldo, void *stream);
+int w8a8_fp8_tile_count(void);
+int w8a8_fp8_tile_auto(int64_t M, int64_t N, int64_t K);
+
 /* Number of tile configurations, a short name of one, and the tile the
  * automatic choice picks for a shape. Main kernel: "128x192/m1n2k2/l23" is
  * tile rows x columns / wave row groups, column groups and k-groups / token

@@ -61,7 +61,7 @@ class Oracle:
             "oracle_fp8_quant_rows_bf16": [vp, i64, i64, i64, vp, i64, vp],
             "oracle_fp8_quant_rows_f32": [vp, i64, i64, i64, vp, i64, vp],
             "oracle_fp8_gemm_rows": [vp, i64, vp, i64, vp, i64, i64, i64, vp, i64],
-            "oracle_fp8_epilogue": [vp, i64, i64, i64, vp, vp, vp, vp, vp, i64],
+            "oracle_fp8_epilogue": [vp, i64, i64, i64, vp, vp, vp, vp, vp, i64, ctypes.c_int],
         }.items():
             fn = getattr(lib, name)
             fn.argtypes = args
@@ -215,9 +215,10 @@ class Oracle:
                     "fp8_gemm")
         return acc
 
-    def fp8_epilogue(self, acc, xs, ws, bias=None) -> Tuple[np.ndarray, np.ndarray]:
-        """(bf16 bits of the fp32-order epilogue on fl32(acc), bf16 bits of the
-        fp64 value rounded once)."""
+    def fp8_epilogue(self, acc, xs, ws, bias=None, f16: bool = False
+                     ) -> Tuple[np.ndarray, np.ndarray]:
+        """(bits of the fp32-order epilogue on fl32(acc), bits of the fp64 value
+        rounded once): bf16, or fp16 (with an fp16 bias) when f16."""
         acc = np.ascontiguousarray(acc, dtype=np.float64)
         xs = np.ascontiguousarray(xs, dtype=np.float32)
         ws = np.ascontiguousarray(ws, dtype=np.float32)
@@ -226,7 +227,7 @@ class Oracle:
         o32 = np.empty((M, N), dtype=np.uint16)
         o64 = np.empty((M, N), dtype=np.uint16)
         self._check(self.lib.oracle_fp8_epilogue(_p(acc), N, M, N, _p(xs), _p(ws), _p(b), _p(o32),
-                                                 _p(o64), N), "fp8_epilogue")
+                                                 _p(o64), N, int(f16)), "fp8_epilogue")
         return o32, o64
 
     def double_to_e4m3(self, d: float) -> int:

@@ -489,11 +489,11 @@ int oracle_fp8_gemm_rows(const uint8_t *a, int64_t lda, const int64_t *rows, int
 }
 
 /* The epilogue on exact accumulators: fl32(acc), then the fp32 order of
- * oracle_epilogue_f32 (bf16 bias and output); and the fp64 value rounded
- * once, the tolerance reference. */
+ * oracle_epilogue_f32; and the fp64 value rounded once, the tolerance
+ * reference. Bias and outputs are bf16 bits, or fp16 bits when f16. */
 int oracle_fp8_epilogue(const double *acc, int64_t ldc, int64_t M, int64_t N, const float *xs,
                         const float *ws, const uint16_t *bias, uint16_t *out32, uint16_t *out64,
-                        int64_t ldo)
+                        int64_t ldo, int f16)
 {
     if (M < 0 || N < 1 || ldc < N || ldo < N ||
         (M > 0 && (!acc || !xs || !ws || !out32 || !out64)))
@@ -502,16 +502,18 @@ int oracle_fp8_epilogue(const double *acc, int64_t ldc, int64_t M, int64_t N, co
 #pragma omp parallel for schedule(static)
     for (m = 0; m < M; ++m) {
         for (int64_t n = 0; n < N; ++n) {
+            const float b = !bias ? 0.0f : f16 ? f16_bits_to_float(bias[n])
+                                                : bf16_bits_to_float(bias[n]);
             float t = (float)acc[m * ldc + n];
             t = t * xs[m];
             t = t * ws[n];
             if (bias)
-                t = t + bf16_bits_to_float(bias[n]);
-            out32[m * ldo + n] = float_to_bf16_rne(t);
+                t = t + b;
+            out32[m * ldo + n] = f16 ? double_to_f16_rne((double)t) : float_to_bf16_rne(t);
             double d = acc[m * ldc + n] * (double)xs[m] * (double)ws[n];
             if (bias)
-                d += (double)bf16_bits_to_float(bias[n]);
-            out64[m * ldo + n] = double_to_bf16_rne(d);
+                d += (double)b;
+            out64[m * ldo + n] = f16 ? double_to_f16_rne(d) : double_to_bf16_rne(d);
         }
     }
     return ORACLE_OK;

@@ -478,6 +478,15 @@ def pin_fp8_epilogue(o):
                 assert o64[m, n] == _exact_bf16(v), (m, n)
                 t = np.float32(acc[m, n]) * xs[m] * ws[n]
                 assert abs(int(o32[m, n]) - int(o64[m, n])) <= 1 or np.sign(t) == 0
+    # fp16 bias and outputs
+    b16 = (rng.standard_normal(N) * 0.01).astype(np.float16).view(np.uint16)
+    o32, o64 = o.fp8_epilogue(acc, xs, ws, b16, f16=True)
+    for m in range(M):
+        for n in range(N):
+            v = Fraction(float(acc[m, n])) * Fraction(float(xs[m])) * Fraction(float(ws[n]))
+            v += Fraction(float(np.array([b16[n]], np.uint16).view(np.float16)[0]))
+            assert o64[m, n] == _exact_f16(v), (m, n)
+            assert abs(int(o32[m, n]) - int(o64[m, n])) <= 1
 
 
 # ---------------------------------------------------------------------------

@@ -45,6 +45,17 @@ SIGNATURES = {
                                         _int, _vp, _i64, _vp]),
     "int8_quant_scaled_mm_f16_tile": (_int, [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64,
                                              _i64, _int, _vp, _i64, _vp, _int]),
+    "fp8_quant_per_token": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
+    "fp8_quant_per_channel": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
+    "fp8_quant_prepack_weight": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "fp8_scaled_mm": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _i64,
+                             _vp]),
+    "fp8_scaled_mm_tile": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp,
+                                  _i64, _vp, _int]),
+    "fp8_quant_scaled_mm": (_int, [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                   _int, _vp, _i64, _vp]),
+    "w8a8_fp8_tile_count": (_int, []),
+    "w8a8_fp8_tile_auto": (_int, [_i64, _i64, _i64]),
     "w8a8_mm_tile_count": (_int, []),
     "w8a8_mm_tile_name": (ctypes.c_char_p, [_int]),
     "w8a8_mm_tile_auto": (_int, [_i64, _i64, _i64]),

@@ -24,7 +24,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIBRARY = os.path.join(HERE, "libw8a8.so")
-SOURCES = ["quant.hip", "prepack.hip", "scaled_mm.hip", "skinny_mm.hip", "api.cpp"]
+SOURCES = ["quant.hip", "prepack.hip", "scaled_mm.hip", "scaled_mm_fp8.hip", "skinny_mm.hip", "api.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -85,7 +85,7 @@ w8a8_status_t launched(hipError_t e, const char *what)
 }
 
 w8a8_status_t quant_common(const void *x, int kind, int64_t M, int64_t K, int64_t ldx, int8_t *q,
-                           int64_t ldq, float *s, void *stream, const char *what)
+                           int64_t ldq, float *s, void *stream, const char *what, bool fp8 = false)
 {
     const bool f32 = kind == w8a8::kElemF32;
     if (M < 0 || M > kMaxRows)
@@ -110,7 +110,7 @@ w8a8_status_t quant_common(const void *x, int kind, int64_t M, int64_t K, int64_
     if (st != W8A8_OK)
         return st;
     return launched(w8a8::launch_quant_rows(x, kind, M, K, ldx, q, ldq, s,
-                                            reinterpret_cast<hipStream_t>(stream)),
+                                            reinterpret_cast<hipStream_t>(stream), fp8),
                     what);
 }
 
@@ -222,11 +222,11 @@ namespace {
 w8a8_status_t mm_args(const int8_t *xq, int64_t ldq, const float *x_scale, const void *w_packed,
                       const float *w_scale, const uint16_t *bias, int64_t M, int64_t N, int64_t K,
                       int mode, void *out, int64_t ldo, int tile, bool need_xs, const char *what,
-                      w8a8::MmArgs &a, int &t)
+                      w8a8::MmArgs &a, int &t, bool fp8 = false)
 {
     if (mode != W8A8_OUT_BF16 && mode != W8A8_OUT_I32 && mode != W8A8_OUT_F16)
         return fail(W8A8_ERR_MODE, "%s: unknown output mode %d", what, mode);
-    if (tile < -1 || tile >= w8a8::mm_tile_count())
+    if (tile < -1 || tile >= (fp8 ? w8a8::fp8_tile_count() : w8a8::mm_tile_count()))
         return fail(W8A8_ERR_MODE, "%s: unknown tile %d", what, tile);
     if (M < 0 || M > kMaxRows || N < 1 || N > kMaxRows)
         return fail(W8A8_ERR_SHAPE, "%s: M or N out of range", what);
@@ -249,7 +249,7 @@ w8a8_status_t mm_args(const int8_t *xq, int64_t ldq, const float *x_scale, const
         return fail(W8A8_ERR_ALIGN, "%s: out must be aligned to its element size", what);
     if ((x_scale && !aligned(x_scale, 4)) || (!i32 && (!aligned(w_scale, 4) || (bias && !aligned(bias, 2)))))
         return fail(W8A8_ERR_ALIGN, "%s: scales/bias misaligned", what);
-    t = tile >= 0 ? tile : w8a8::mm_tile_auto(M, N, K);
+    t = tile >= 0 ? tile : fp8 ? w8a8::mm_tile_auto_main(M, N, K) : w8a8::mm_tile_auto(M, N, K);
     a.xq = xq;
     a.xs = (i32 && !need_xs) ? nullptr : x_scale;
     a.wp = reinterpret_cast<const int8_t *>(w_packed);
@@ -391,6 +391,115 @@ W8A8_API w8a8_status_t int8_scaled_mm(const int8_t *xq, int64_t ldq, const float
 {
     return int8_scaled_mm_tile(xq, ldq, x_scale, w_packed, w_scale, bias, M, N, K, mode, out, ldo,
                                stream, -1);
+}
+
+// ---- the FP8 (e4m3) twin ----------------------------------------------
+
+W8A8_API w8a8_status_t fp8_quant_per_token(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                                           uint8_t *xq, int64_t ldq, float *x_scale, void *stream)
+{
+    return quant_common(x, w8a8::kElemBF16, M, K, ldx, reinterpret_cast<int8_t *>(xq), ldq, x_scale,
+                        stream, "fp8_quant_per_token", true);
+}
+
+W8A8_API w8a8_status_t fp8_quant_per_channel(const float *w, int64_t N, int64_t K, int64_t ldw,
+                                             uint8_t *wq, int64_t ldq, float *w_scale,
+                                             void *stream)
+{
+    return quant_common(w, w8a8::kElemF32, N, K, ldw, reinterpret_cast<int8_t *>(wq), ldq, w_scale,
+                        stream, "fp8_quant_per_channel", true);
+}
+
+W8A8_API w8a8_status_t fp8_quant_prepack_weight(const void *w, int w_dtype, int64_t N, int64_t K,
+                                                int64_t ldw, void *w_packed, float *w_scale,
+                                                void *stream)
+{
+    const char *what = "fp8_quant_prepack_weight";
+    if (w_dtype != W8A8_W_F32 && w_dtype != W8A8_W_BF16)
+        return fail(W8A8_ERR_MODE, "%s: unknown weight dtype %d", what, w_dtype);
+    const bool f32 = w_dtype == W8A8_W_F32;
+    w8a8_status_t st = pack_common(N, K, ldw, w, w_packed, w_packed, what, false);
+    if (st != W8A8_OK)
+        return st;
+    if (!w_scale)
+        return fail(W8A8_ERR_NULL, "%s: NULL tensor pointer", what);
+    if (!aligned(w, 16) || ldw % (f32 ? 4 : 8) != 0 || !aligned(w_scale, 4))
+        return fail(W8A8_ERR_ALIGN, "%s: w must be 16-byte aligned with ldw a multiple of %d, "
+                    "w_scale 4-byte aligned", what, f32 ? 4 : 8);
+    st = check_device();
+    if (st != W8A8_OK)
+        return st;
+    return launched(w8a8::launch_quant_prepack(w, f32, N, K, ldw, w_packed, w_scale,
+                                               reinterpret_cast<hipStream_t>(stream), true),
+                    what);
+}
+
+W8A8_API w8a8_status_t fp8_scaled_mm_tile(const uint8_t *xq, int64_t ldq, const float *x_scale,
+                                          const void *w_packed, const float *w_scale,
+                                          const uint16_t *bias, int64_t M, int64_t N, int64_t K,
+                                          int mode, void *out, int64_t ldo, void *stream, int tile)
+{
+    const char *what = "fp8_scaled_mm";
+    w8a8::MmArgs a;
+    int t;
+    w8a8_status_t st = mm_args(reinterpret_cast<const int8_t *>(xq), ldq, x_scale, w_packed,
+                               w_scale, bias, M, N, K, mode, out, ldo, tile, false, what, a, t,
+                               true);
+    if (st != W8A8_OK || M == 0)
+        return st;
+    st = check_device();
+    if (st != W8A8_OK)
+        return st;
+    return launched(w8a8::launch_scaled_mm_fp8(a, mode, t, reinterpret_cast<hipStream_t>(stream)),
+                    what);
+}
+
+W8A8_API w8a8_status_t fp8_scaled_mm(const uint8_t *xq, int64_t ldq, const float *x_scale,
+                                     const void *w_packed, const float *w_scale,
+                                     const uint16_t *bias, int64_t M, int64_t N, int64_t K,
+                                     int mode, void *out, int64_t ldo, void *stream)
+{
+    return fp8_scaled_mm_tile(xq, ldq, x_scale, w_packed, w_scale, bias, M, N, K, mode, out, ldo,
+                              stream, -1);
+}
+
+W8A8_API w8a8_status_t fp8_quant_scaled_mm(const uint16_t *x, int64_t ldx, uint8_t *xq,
+                                           int64_t ldq, float *x_scale, const void *w_packed,
+                                           const float *w_scale, const uint16_t *bias, int64_t M,
+                                           int64_t N, int64_t K, int mode, void *out, int64_t ldo,
+                                           void *stream)
+{
+    const char *what = "fp8_quant_scaled_mm";
+    w8a8::MmArgs a;
+    int t;
+    w8a8_status_t st = mm_args(reinterpret_cast<const int8_t *>(xq), ldq, x_scale, w_packed,
+                               w_scale, bias, M, N, K, mode, out, ldo, -1, true, what, a, t, true);
+    if (st != W8A8_OK)
+        return st;
+    if (ldx < K)
+        return fail(W8A8_ERR_SHAPE, "%s: ldx smaller than K", what);
+    if (M == 0)
+        return ok();
+    if (!x)
+        return fail(W8A8_ERR_NULL, "%s: NULL tensor pointer", what);
+    if (!aligned(x, 16) || ldx % 8 != 0)
+        return fail(W8A8_ERR_ALIGN, "%s: x must be 16-byte aligned with ldx a multiple of 8", what);
+    st = check_device();
+    if (st != W8A8_OK)
+        return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t err = w8a8::launch_quant_rows(x, w8a8::kElemBF16, M, K, ldx,
+                                             reinterpret_cast<int8_t *>(xq), ldq, x_scale, s, true);
+    if (err != hipSuccess)
+        return launched(err, what);
+    return launched(w8a8::launch_scaled_mm_fp8(a, mode, t, s), what);
+}
+
+W8A8_API int w8a8_fp8_tile_count(void) { return w8a8::fp8_tile_count(); }
+
+W8A8_API int w8a8_fp8_tile_auto(int64_t M, int64_t N, int64_t K)
+{
+    return w8a8::mm_tile_auto_main(M, N, K);
 }
 
 W8A8_API int w8a8_mm_tile_count(void) { return w8a8::mm_tile_count(); }

@@ -19,9 +19,11 @@ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 constexpr int kElemBF16 = 0, kElemF32 = 1, kElemF16 = 2;
 
 // ---- per-row quantization (quant.hip) ----
-// kind: x is bf16 bits, fp32 or fp16 bits [rows, ldx].
+// kind: x is bf16 bits, fp32 or fp16 bits [rows, ldx]. fp8: e4m3 codes
+// (bf16 or fp32 rows only) instead of int8.
 hipError_t launch_quant_rows(const void *x, int kind, int64_t rows, int64_t K, int64_t ldx,
-                             int8_t *q, int64_t ldq, float *scale, hipStream_t stream);
+                             int8_t *q, int64_t ldq, float *scale, hipStream_t stream,
+                             bool fp8 = false);
 
 // ---- weight repack (prepack.hip) ----
 hipError_t launch_prepack(const int8_t *wq, int64_t N, int64_t K, int64_t ldw, void *packed,
@@ -31,7 +33,8 @@ hipError_t launch_unpack(const void *packed, int64_t N, int64_t K, int8_t *wq, i
 // Per-channel quant of a bf16 (w_f32 false) or fp32 weight [N, ldw] straight
 // into the packed layout, with the fp32 scales.
 hipError_t launch_quant_prepack(const void *w, bool w_f32, int64_t N, int64_t K, int64_t ldw,
-                                void *packed, float *w_scale, hipStream_t stream);
+                                void *packed, float *w_scale, hipStream_t stream,
+                                bool fp8 = false);
 
 // ---- scaled matmul (scaled_mm.hip) ----
 struct MmArgs {
@@ -93,6 +96,14 @@ __device__ __forceinline__ int xcd_remap(int pid, int tiles)
 int mm_tile_count();
 const char *mm_tile_name(int tile);
 int mm_tile_auto(int64_t M, int64_t N, int64_t K);
+// The automatic choice among the main kernel's tiles only (numbers
+// 0 .. fp8_tile_count()-1, the tiles of the e4m3 twin).
+int mm_tile_auto_main(int64_t M, int64_t N, int64_t K);
+
+// ---- the e4m3 twin of the matmul (scaled_mm_fp8.hip) ----
+// mode kOutI32 stores the raw fp32 accumulators.
+int fp8_tile_count();
+hipError_t launch_scaled_mm_fp8(const MmArgs &a, int mode, int tile, hipStream_t stream);
 hipError_t launch_scaled_mm(const MmArgs &a, int mode, int tile, hipStream_t stream);
 // Fused quant + matmul in one launch. Returns hipErrorNotSupported (nothing
 // launched) when the shape's workgroups cannot all be resident at once; the

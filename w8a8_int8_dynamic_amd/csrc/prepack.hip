@@ -13,7 +13,8 @@
 // "Online Quantization", Overview: weights and scales computed while the
 // model loads, from a BF16 or FP32 checkpoint): the per-output-channel rule
 // of quant.hip applied to a bf16 or fp32 weight and written straight into
-// the fragment layout above, so the int8 weight never exists unpacked.
+// the fragment layout above, so the int8 weight never exists unpacked (or,
+// for the e4m3 twin, the same with e4m3 codes and scale absmax / 448).
 #include "internal.hpp"
 #include "quant_rule.hpp"
 
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint4 *__restrict__ p
 // weights of one row, re-read (from L2) and quantized with the row's
 // scale. Rows past N and columns past K give zero codes (load_chunk
 // zero-fills past K; code(0) = 0).
-template <bool F32>
+template <bool F32, bool FP8>
 __global__ __launch_bounds__(256) void quant_prepack_kernel(const char *__restrict__ w, int N, int K,
                                                             int64_t ldw, uint4 *__restrict__ packed,
                                                             float *__restrict__ w_scale, int kblocks)
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(256) void quant_prepack_kernel(const char *__restri
 
     const int l = lane, r = l & 15, n = nb * 16 + r;
     float sc, inv;
-    scale_of(rowmax[r], F32, sc, inv);
+    scale_of(rowmax[r], F32, sc, inv, FP8);
     if (threadIdx.x < 16 && nb * 16 + (int)threadIdx.x < N)
         w_scale[nb * 16 + threadIdx.x] = sc;
     const char *row = w + (int64_t)min(n, N - 1) * ldw * B;
@@ -113,12 +114,13 @@ __global__ __launch_bounds__(256) void quant_prepack_kernel(const char *__restri
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     u32 hi;
-                    chunk_codes<true>(load_chunk<true>(row, k0 + 4 * c, K), inv, q[c], hi);
+                    chunk_codes<kF32, FP8>(load_chunk<true>(row, k0 + 4 * c, K), inv, q[c], hi);
                 }
             } else {
 #pragma unroll
                 for (int c = 0; c < 2; ++c)
-                    chunk_codes<false>(load_chunk<false>(row, k0 + 8 * c, K), inv, q[2 * c], q[2 * c + 1]);
+                    chunk_codes<kBF16, FP8>(load_chunk<false>(row, k0 + 8 * c, K), inv, q[2 * c],
+                                            q[2 * c + 1]);
             }
         }
         packed[((int64_t)nb * kblocks + kb) * 64 + l] = make_uint4(q[0], q[1], q[2], q[3]);
@@ -128,11 +130,12 @@ __global__ __launch_bounds__(256) void quant_prepack_kernel(const char *__restri
 }  // namespace
 
 hipError_t launch_quant_prepack(const void *w, bool w_f32, int64_t N, int64_t K, int64_t ldw,
-                                void *packed, float *w_scale, hipStream_t stream)
+                                void *packed, float *w_scale, hipStream_t stream, bool fp8)
 {
     const int64_t kblocks = ceil_div(K, kFragK);
     const int64_t nblocks = ceil_div(N, kFragN);
-    hipLaunchKernelGGL(w_f32 ? quant_prepack_kernel<true> : quant_prepack_kernel<false>,
+    hipLaunchKernelGGL(w_f32 ? (fp8 ? quant_prepack_kernel<true, true> : quant_prepack_kernel<true, false>)
+                             : (fp8 ? quant_prepack_kernel<false, true> : quant_prepack_kernel<false, false>),
                        dim3((unsigned)nblocks), dim3(256), 0, stream, reinterpret_cast<const char *>(w),
                        (int)N, (int)K, ldw, reinterpret_cast<uint4 *>(packed), w_scale, (int)kblocks);
     return hipGetLastError();

@@ -21,6 +21,8 @@
 //     row_half_mirror, row_mirror) and four readlanes; the WPR partials of
 //     a row meet in LDS.
 //   - Codes are written 8 (bf16, fp16) or 4 (fp32) per lane per chunk.
+//   - The FP8 instantiations write e4m3 codes with scale absmax / 448 (the
+//     e4m3 twin of the layer; bf16 activations and fp32 weights).
 //   - The row loads of the single-pass kernel and all code stores are
 //     nontemporal: each byte is touched once, and keeping it out of the
 //     caches lifts HBM throughput.
@@ -37,7 +39,7 @@ namespace {
 using namespace quant_rule;
 
 // Register-resident kernel: CH chunks per lane, WPR waves per row, 4 waves per block.
-template <int E, int CH, int WPR>
+template <int E, int CH, int WPR, bool FP8>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void *__restrict__ x, int64_t rows,
                                                          int K, int64_t ldx,
                                                          int8_t *__restrict__ q, int64_t ldq,
@@ -77,7 +79,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void *__restrict_
     if (!valid)
         return;
     float s, inv;
-    scale_of(m, E, s, inv);
+    scale_of(m, E, s, inv, FP8);
     if (wr == 0 && lane == 0)
         scale[row] = s;
     int8_t *qrow = q + row * ldq;
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void *__restrict_
         const int64_t e = ((int64_t)(c * WPR + wr) * 64 + lane) * VEC;
         if (e < K) {
             u32 lo, hi;
-            chunk_codes<E>(v[c], inv, lo, hi);
+            chunk_codes<E, FP8>(v[c], inv, lo, hi);
             store_codes<E>(qrow, e, K, lo, hi);
         }
     }
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void *__restrict_
 
 // Two-pass kernel for rows longer than the register-resident limit:
 // one row per block of 4 waves; pass 1 finds the absmax, pass 2 re-reads.
-template <int E>
+template <int E, bool FP8>
 __global__ __launch_bounds__(256) void quant_rows_looped_kernel(const void *__restrict__ x,
                                                                 int64_t rows, int K, int64_t ldx,
                                                                 int8_t *__restrict__ q, int64_t ldq,
@@ -116,13 +118,13 @@ __global__ __launch_bounds__(256) void quant_rows_looped_kernel(const void *__re
     __syncthreads();
     m = max(max(part[0], part[1]), max(part[2], part[3]));
     float s, inv;
-    scale_of(m, E, s, inv);
+    scale_of(m, E, s, inv, FP8);
     if (threadIdx.x == 0)
         scale[row] = s;
     int8_t *qrow = q + row * ldq;
     for (int64_t e = (int64_t)threadIdx.x * VEC; e < K; e += step) {
         u32 lo, hi;
-        chunk_codes<E>(load_chunk<E>(xrow, e, K), inv, lo, hi);
+        chunk_codes<E, FP8>(load_chunk<E>(xrow, e, K), inv, lo, hi);
         store_codes<E>(qrow, e, K, lo, hi);
     }
 }
@@ -133,35 +135,35 @@ constexpr int kChOptions[] = {1, 2, 3, 4, 6, 8, 12, 16};
 constexpr int kNumCh = sizeof(kChOptions) / sizeof(kChOptions[0]);
 constexpr int kWprOptions[] = {1, 2, 4};
 
-template <int E, int WPR>
+template <int E, int WPR, bool FP8>
 QuantFn pick_ch(int idx)
 {
     switch (idx) {
-    case 0: return quant_rows_kernel<E, 1, WPR>;
-    case 1: return quant_rows_kernel<E, 2, WPR>;
-    case 2: return quant_rows_kernel<E, 3, WPR>;
-    case 3: return quant_rows_kernel<E, 4, WPR>;
-    case 4: return quant_rows_kernel<E, 6, WPR>;
-    case 5: return quant_rows_kernel<E, 8, WPR>;
-    case 6: return quant_rows_kernel<E, 12, WPR>;
-    default: return quant_rows_kernel<E, 16, WPR>;
+    case 0: return quant_rows_kernel<E, 1, WPR, FP8>;
+    case 1: return quant_rows_kernel<E, 2, WPR, FP8>;
+    case 2: return quant_rows_kernel<E, 3, WPR, FP8>;
+    case 3: return quant_rows_kernel<E, 4, WPR, FP8>;
+    case 4: return quant_rows_kernel<E, 6, WPR, FP8>;
+    case 5: return quant_rows_kernel<E, 8, WPR, FP8>;
+    case 6: return quant_rows_kernel<E, 12, WPR, FP8>;
+    default: return quant_rows_kernel<E, 16, WPR, FP8>;
     }
 }
 
-template <int E>
+template <int E, bool FP8>
 QuantFn pick(int wpr, int ch_idx)
 {
     switch (wpr) {
-    case 1: return pick_ch<E, 1>(ch_idx);
-    case 2: return pick_ch<E, 2>(ch_idx);
-    default: return pick_ch<E, 4>(ch_idx);
+    case 1: return pick_ch<E, 1, FP8>(ch_idx);
+    case 2: return pick_ch<E, 2, FP8>(ch_idx);
+    default: return pick_ch<E, 4, FP8>(ch_idx);
     }
 }
 
 }  // namespace
 
 hipError_t launch_quant_rows(const void *x, int kind, int64_t rows, int64_t K, int64_t ldx,
-                             int8_t *q, int64_t ldq, float *scale, hipStream_t stream)
+                             int8_t *q, int64_t ldq, float *scale, hipStream_t stream, bool fp8)
 {
     if (rows == 0)
         return hipSuccess;
@@ -184,14 +186,17 @@ hipError_t launch_quant_rows(const void *x, int kind, int64_t rows, int64_t K, i
         if (wpr < 4 && need > 1 && rows * wpr < kEnoughWaves)
             continue;
         const int rpb = 4 / wpr;
-        QuantFn fn = kind == kF32 ? pick<kF32>(wpr, ch_idx)
-                   : kind == kF16 ? pick<kF16>(wpr, ch_idx) : pick<kBF16>(wpr, ch_idx);
+        QuantFn fn = fp8 ? (kind == kF32 ? pick<kF32, true>(wpr, ch_idx) : pick<kBF16, true>(wpr, ch_idx))
+                   : kind == kF32 ? pick<kF32, false>(wpr, ch_idx)
+                   : kind == kF16 ? pick<kF16, false>(wpr, ch_idx) : pick<kBF16, false>(wpr, ch_idx);
         hipLaunchKernelGGL(fn, dim3((unsigned)ceil_div(rows, rpb)), dim3(256), 0, stream, x, rows,
                            (int)K, ldx, q, ldq, scale);
         return hipGetLastError();
     }
-    QuantFn fn = kind == kF32 ? quant_rows_looped_kernel<kF32>
-               : kind == kF16 ? quant_rows_looped_kernel<kF16> : quant_rows_looped_kernel<kBF16>;
+    QuantFn fn = fp8 ? (kind == kF32 ? quant_rows_looped_kernel<kF32, true>
+                              : quant_rows_looped_kernel<kBF16, true>)
+               : kind == kF32 ? quant_rows_looped_kernel<kF32, false>
+               : kind == kF16 ? quant_rows_looped_kernel<kF16, false> : quant_rows_looped_kernel<kBF16, false>;
     hipLaunchKernelGGL(fn, dim3((unsigned)rows), dim3(256), 0, stream, x, rows, (int)K, ldx, q,
                        ldq, scale);
     return hipGetLastError();

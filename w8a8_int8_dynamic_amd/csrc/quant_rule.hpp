@@ -78,26 +78,49 @@ __device__ __forceinline__ u32 code(float f, float inv)
     return (u32)((int)t) & 0xffu;
 }
 
+// The e4m3 twin's code (OCP e4m3: 4 exponent bits, bias 7, 3 mantissa
+// bits, largest finite 448): t = clamp(fl32(f*inv), -448, 448) rounded to
+// the nearest e4m3 value, ties to even, the sign kept (zeros included).
+// From 2^-6 up the fp32 pattern is rounded to 3 mantissa bits (a carry
+// moves into the exponent) and rebiased; below, the step is 2^-9 and the
+// code is rint(|t| * 2^9).
+__device__ __forceinline__ u32 code_fp8(float f, float inv)
+{
+    const float t = fminf(fmaxf(f * inv, -448.0f), 448.0f);
+    const u32 u = __float_as_uint(t);
+    const u32 a = u & 0x7fffffffu;
+    const u32 mag = a < 0x3c800000u ? (u32)__builtin_rintf(__uint_as_float(a) * 512.0f)
+                                    : ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+    return (u >> 24 & 0x80u) | mag;
+}
+
+template <bool FP8>
+__device__ __forceinline__ u32 code_of(float f, float inv)
+{
+    return FP8 ? code_fp8(f, inv) : code(f, inv);
+}
+
 // Codes of one chunk: bf16 or fp16 -> 8 codes in (lo, hi); fp32 -> 4 codes
-// in lo.
-template <int E>
+// in lo. FP8: e4m3 codes instead of int8.
+template <int E, bool FP8 = false>
 __device__ __forceinline__ void chunk_codes(const uint4 &v, float inv, u32 &lo, u32 &hi)
 {
     const u32 d[4] = {v.x, v.y, v.z, v.w};
     if (E == kF32) {
-        lo = code(__uint_as_float(d[0]), inv) | code(__uint_as_float(d[1]), inv) << 8 |
-             code(__uint_as_float(d[2]), inv) << 16 | code(__uint_as_float(d[3]), inv) << 24;
+        lo = code_of<FP8>(__uint_as_float(d[0]), inv) | code_of<FP8>(__uint_as_float(d[1]), inv) << 8 |
+             code_of<FP8>(__uint_as_float(d[2]), inv) << 16 |
+             code_of<FP8>(__uint_as_float(d[3]), inv) << 24;
         hi = 0;
     } else {
         u32 c[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (E == kF16) {
-                c[2 * i] = code(f16_to_float(d[i]), inv);
-                c[2 * i + 1] = code(f16_to_float(d[i] >> 16), inv);
+                c[2 * i] = code_of<FP8>(f16_to_float(d[i]), inv);
+                c[2 * i + 1] = code_of<FP8>(f16_to_float(d[i] >> 16), inv);
             } else {
-                c[2 * i] = code(__uint_as_float(d[i] << 16), inv);
-                c[2 * i + 1] = code(__uint_as_float(d[i] & 0xffff0000u), inv);
+                c[2 * i] = code_of<FP8>(__uint_as_float(d[i] << 16), inv);
+                c[2 * i + 1] = code_of<FP8>(__uint_as_float(d[i] & 0xffff0000u), inv);
             }
         }
         lo = c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24;
@@ -152,16 +175,20 @@ __device__ __forceinline__ void store_codes(int8_t *qrow, int64_t e, int K, u32 
             qrow[e + j] = (int8_t)((j < 4 ? lo >> (8 * j) : hi >> (8 * (j - 4))) & 0xffu);
 }
 
-// Scale and reciprocal of a row from its absmax bit pattern m (kind e).
-__device__ __forceinline__ void scale_of(u32 m, int e, float &s, float &inv)
+// Scale and reciprocal of a row from its absmax bit pattern m (kind e):
+// absmax / 127 for int8 codes, absmax / 448 for the e4m3 twin.
+__device__ __forceinline__ void scale_of(u32 m, int e, float &s, float &inv, bool fp8 = false)
 {
-    const float a = e == kF32 ? __uint_as_float(m) : e == kF16 ? f16_to_float(m) : __uint_as_float(m << 16);
+    const float a = e == kF32   ? __uint_as_float(m)
+                    : e == kF16 ? f16_to_float(m)
+                                : __uint_as_float(m << 16);
+    const float qmax = fp8 ? 448.0f : 127.0f;
     if (a < 0x1p-100f) {
         s = 0.0f;
         inv = 0.0f;                      // x * 0 -> code 0 for every element
     } else {
-        s = a / 127.0f;                  // correctly rounded fp32 divide
-        inv = 127.0f / a;
+        s = a / qmax;                    // correctly rounded fp32 divide
+        inv = qmax / a;
     }
 }
 

@@ -17,7 +17,8 @@ from ._lib import W8A8_OUT_BF16, W8A8_OUT_F16, W8A8_OUT_I32, call
 
 __all__ = ["quant_per_token", "quant_per_channel", "prepack_weight", "quant_prepack_weight", "unpack_weight",
            "prepack_weight_bytes", "scaled_mm", "quant_scaled_mm", "tile_count", "tile_name",
-           "tile_auto", "device_supported"]
+           "tile_auto", "device_supported", "fp8_quant_per_token", "fp8_quant_per_channel",
+           "fp8_quant_prepack_weight", "fp8_scaled_mm", "fp8_quant_scaled_mm", "fp8_tile_count"]
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -236,6 +237,120 @@ def quant_scaled_mm(x: torch.Tensor, w_packed: torch.Tensor, ws: Optional[torch.
              xq.data_ptr(), _ld(xq), xs.data_ptr(), w_packed.data_ptr(), ptr(ws), ptr(bias), M,
              N, K, mode, out.data_ptr(), _ld(out), _stream(x), tile)
     return out, xq, xs
+
+
+# ---- the FP8 (e4m3) twin ------------------------------------------------
+_FP8_OUT_MODE = {torch.bfloat16: W8A8_OUT_BF16, torch.float16: W8A8_OUT_F16,
+                 torch.float32: W8A8_OUT_I32}
+
+
+def _fp8_codes(M: int, K: int, device) -> torch.Tensor:
+    return torch.empty((M, _round_up(K, 16)), dtype=torch.uint8, device=device)[:, :K]
+
+
+def fp8_quant_per_token(x: torch.Tensor, xq: Optional[torch.Tensor] = None,
+                        xs: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-token dynamic e4m3 quantization of bf16 x [M, K] -> (uint8 codes [M, K], fp32 [M])."""
+    _matrix(x, "x", torch.bfloat16)
+    M, K = x.shape
+    x = _rows_aligned(x, 8)
+    xq = _fp8_codes(M, K, x.device) if xq is None else xq
+    xs = torch.empty((M,), dtype=torch.float32, device=x.device) if xs is None else xs
+    _matrix(xq, "xq", torch.uint8)
+    _vector(xs, M, "xs", torch.float32)
+    with torch.cuda.device(x.device):
+        call("fp8_quant_per_token", x.data_ptr(), M, K, _ld(x), xq.data_ptr(), _ld(xq),
+             xs.data_ptr(), _stream(x))
+    return xq, xs
+
+
+def fp8_quant_per_channel(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-output-channel e4m3 quantization of fp32 w [N, K] -> (uint8 [N, K], fp32 [N])."""
+    _matrix(w, "w", torch.float32)
+    N, K = w.shape
+    w = _rows_aligned(w, 4)
+    wq = _fp8_codes(N, K, w.device)
+    ws = torch.empty((N,), dtype=torch.float32, device=w.device)
+    with torch.cuda.device(w.device):
+        call("fp8_quant_per_channel", w.data_ptr(), N, K, _ld(w), wq.data_ptr(), _ld(wq),
+             ws.data_ptr(), _stream(w))
+    return wq, ws
+
+
+def fp8_quant_prepack_weight(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Online e4m3 quantization of a bf16 or fp32 weight [N, K] into the packed layout."""
+    if w.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"w must be bfloat16 or float32, got {w.dtype}")
+    _matrix(w, "w", w.dtype)
+    N, K = w.shape
+    f32 = w.dtype == torch.float32
+    w = _rows_aligned(w, 4 if f32 else 8)
+    packed = torch.empty((prepack_weight_bytes(N, K),), dtype=torch.uint8, device=w.device)
+    ws = torch.empty((N,), dtype=torch.float32, device=w.device)
+    with torch.cuda.device(w.device):
+        call("fp8_quant_prepack_weight", w.data_ptr(), 0 if f32 else 1, N, K, _ld(w),
+             packed.data_ptr(), ws.data_ptr(), _stream(w))
+    return packed, ws
+
+
+def fp8_scaled_mm(xq: torch.Tensor, xs: Optional[torch.Tensor], w_packed: torch.Tensor,
+                  ws: Optional[torch.Tensor], N: int, bias: Optional[torch.Tensor] = None,
+                  out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                  tile: int = -1) -> torch.Tensor:
+    """The e4m3 twin of scaled_mm: xq uint8 e4m3 codes; out_dtype bf16 or fp16 (bias
+    of that type), or float32 for the raw fp32 accumulators."""
+    _matrix(xq, "xq", torch.uint8)
+    M, K = xq.shape
+    if out_dtype not in _FP8_OUT_MODE:
+        raise TypeError("out_dtype must be torch.bfloat16, torch.float16 or torch.float32")
+    mode = _FP8_OUT_MODE[out_dtype]
+    if mode != W8A8_OUT_I32:
+        _vector(xs, M, "xs", torch.float32)
+        _vector(ws, N, "ws", torch.float32)
+        _vector(bias, N, "bias", out_dtype)
+    if not w_packed.is_cuda or w_packed.dtype != torch.uint8 or \
+            w_packed.numel() < prepack_weight_bytes(N, K):
+        raise ValueError("w_packed must be a uint8 device buffer of the packed layout (N, K)")
+    out = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
+    _matrix(out, "out", out_dtype)
+    if out.shape != (M, N):
+        raise ValueError(f"out must have shape {(M, N)}")
+
+    def ptr(t):
+        return None if t is None or mode == W8A8_OUT_I32 else t.data_ptr()
+
+    with torch.cuda.device(xq.device):
+        call("fp8_scaled_mm_tile", xq.data_ptr(), _ld(xq), ptr(xs), w_packed.data_ptr(), ptr(ws),
+             ptr(bias), M, N, K, mode, out.data_ptr(), _ld(out), _stream(xq), tile)
+    return out
+
+
+def fp8_quant_scaled_mm(x: torch.Tensor, w_packed: torch.Tensor, ws: torch.Tensor, N: int,
+                        bias: Optional[torch.Tensor] = None,
+                        out_dtype: torch.dtype = torch.bfloat16,
+                        out: Optional[torch.Tensor] = None
+                        ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """e4m3 per-token quant of bf16 x and the e4m3 scaled matmul: (out, xq, xs)."""
+    _matrix(x, "x", torch.bfloat16)
+    M, K = x.shape
+    x = _rows_aligned(x, 8)
+    if out_dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float16")
+    _vector(ws, N, "ws", torch.float32)
+    _vector(bias, N, "bias", out_dtype)
+    xq = _fp8_codes(M, K, x.device)
+    xs = torch.empty((M,), dtype=torch.float32, device=x.device)
+    out = torch.empty((M, N), dtype=out_dtype, device=x.device) if out is None else out
+    _matrix(out, "out", out_dtype)
+    with torch.cuda.device(x.device):
+        call("fp8_quant_scaled_mm", x.data_ptr(), _ld(x), xq.data_ptr(), _ld(xq), xs.data_ptr(),
+             w_packed.data_ptr(), ws.data_ptr(), None if bias is None else bias.data_ptr(), M, N,
+             K, _FP8_OUT_MODE[out_dtype], out.data_ptr(), _ld(out), _stream(x))
+    return out, xq, xs
+
+
+def fp8_tile_count() -> int:
+    return _lib.lib().w8a8_fp8_tile_count()
 
 
 def tile_count() -> int:
