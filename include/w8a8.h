@@ -294,18 +294,25 @@ w8a8_status_t fp8_scaled_mm(const uint8_t *xq, int64_t ldq, const float *x_scale
                             const void *w_packed, const float *w_scale, const uint16_t *bias,
                             int64_t M, int64_t N, int64_t K, int mode, void *out, int64_t ldo,
                             void *stream);
-/* fp8_scaled_mm with an explicit tile (0 <= tile < w8a8_fp8_tile_count(), the
- * main kernel's configurations, named by w8a8_mm_tile_name) or -1. */
+/* fp8_scaled_mm with an explicit tile (0 <= tile < w8a8_fp8_tile_count(): the
+ * int8 configurations, same numbers and names, main and small-M) or -1. */
 w8a8_status_t fp8_scaled_mm_tile(const uint8_t *xq, int64_t ldq, const float *x_scale,
                                  const void *w_packed, const float *w_scale, const uint16_t *bias,
                                  int64_t M, int64_t N, int64_t K, int mode, void *out, int64_t ldo,
                                  void *stream, int tile);
-/* fp8_quant_per_token of bf16 x, then fp8_scaled_mm (two launches), writing
- * xq and x_scale too. */
+/* fp8_quant_per_token of bf16 x, then fp8_scaled_mm, writing xq and x_scale
+ * too; in one launch where int8_quant_scaled_mm would use one (modes
+ * W8A8_OUT_BF16 and W8A8_OUT_I32), else two. */
 w8a8_status_t fp8_quant_scaled_mm(const uint16_t *x, int64_t ldx, uint8_t *xq, int64_t ldq,
                                   float *x_scale, const void *w_packed, const float *w_scale,
                                   const uint16_t *bias, int64_t M, int64_t N, int64_t K, int mode,
                                   void *out, int64_t ldo, void *stream);
+/* fp8_quant_scaled_mm with an explicit tile (or -1). */
+w8a8_status_t fp8_quant_scaled_mm_tile(const uint16_t *x, int64_t ldx, uint8_t *xq, int64_t ldq,
+                                       float *x_scale, const void *w_packed,
+                                       const float *w_scale, const uint16_t *bias, int64_t M,
+                                       int64_t N, int64_t K, int mode, void *out, int64_t ldo,
+                                       void *stream, int tile);
 int w8a8_fp8_tile_count(void);
 int w8a8_fp8_tile_auto(int64_t M, int64_t N, int64_t K);
 

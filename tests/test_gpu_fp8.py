@@ -194,6 +194,36 @@ def test_fp8_quant_scaled_mm_and_f16_out(ops, orc):
     assert np.array_equal(bits_np(out16), own16)
 
 
+QMM_SHAPES = [(1, 48, 64), (2, 1000, 4112), (37, 45, 80), (257, 300, 1040), (512, 1536, 512)]
+
+
+@pytest.mark.parametrize("M,N,K", QMM_SHAPES)
+def test_fp8_quant_scaled_mm_every_tile(ops, orc, M, N, K):
+    """fp8_quant_scaled_mm for every tile (the single-launch main and small-M
+    paths with e4m3 producers, and the two-launch fallback), twice per tile:
+    codes and scales bit-exact, raw accumulators within the bound, bf16
+    outputs bit-exact to the epilogue on those accumulators."""
+    inp = wl.random_case(M, K, N, 8500 + M + N + K, bias=True)
+    x = bf16_dev(inp.x_bf16)
+    wq, ws_ref = orc.fp8_quant_per_channel(inp.w_f32)
+    packed, ws = ops.fp8_quant_prepack_weight(torch.from_numpy(inp.w_f32).to(DEV))
+    b = bf16_dev(inp.bias_bf16)
+    xq_ref, xs_ref = orc.fp8_quant_per_token(inp.x_bf16)
+    exact = orc.fp8_gemm(xq_ref, wq)
+    for t in range(ops.fp8_tile_count()):
+        name = ops.tile_name(t)
+        acc, xq, xs = ops.fp8_quant_scaled_mm(x, packed, None, N, out_dtype=torch.float32, tile=t)
+        assert np.array_equal(xq.cpu().numpy(), xq_ref) and np.array_equal(xs.cpu().numpy(), xs_ref), name
+        acc = acc.cpu().numpy()
+        check_acc(orc, acc, xq_ref, wq, exact, name)
+        own32, _ = orc.fp8_epilogue(acc.astype(np.float64), xs_ref, ws_ref, inp.bias_bf16)
+        for _ in range(2):
+            out, xq, xs = ops.fp8_quant_scaled_mm(x, packed, ws, N, b, tile=t)
+            torch.cuda.synchronize()
+            assert np.array_equal(xq.cpu().numpy(), xq_ref), name
+            assert np.array_equal(bits_np(out), own32), name
+
+
 def test_fp8_full_size_fused_qkv(ops, orc):
     """The fused-QKV workload at full size through the e4m3 twin: codes and
     scales exact; sampled rows' accumulators within the bound and outputs

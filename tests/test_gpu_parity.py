@@ -252,6 +252,35 @@ def test_scaled_mm_decode_shapes_auto(ops, orc, M):
     assert np.array_equal(got.cpu().numpy(), acc)
 
 
+def test_scaled_mm_max_k_extremes(ops, orc):
+    """K = W8A8_MAX_K with codes of magnitude 127 and mostly aligned signs:
+    accumulators reach +-127^2 K (just inside int32) in every tile,
+    main and small-M, exact in int32 and in the bf16 epilogue."""
+    from w8a8_int8_dynamic_amd import _lib
+    K = _lib.W8A8_MAX_K
+    M, N = 33, 40
+    rng = np.random.default_rng(4400)
+    xq = np.where(rng.random((M, K)) < 0.999, 127, -127).astype(np.int8)
+    wq = np.where(rng.random((N, K)) < 0.999, 127, -127).astype(np.int8)
+    xq[0] = 127
+    wq[0] = 127                                  # acc[0, 0] = 127^2 K
+    wq[1] = -127                                 # acc[0, 1] = -127^2 K
+    acc = orc.gemm_i32(xq, wq)
+    assert acc[0, 0] == 127 * 127 * K and acc[0, 1] == -127 * 127 * K
+    xs = rng.uniform(1e-3, 1e-2, M).astype(np.float32)
+    ws = rng.uniform(1e-4, 1e-3, N).astype(np.float32)
+    ref32 = orc.epilogue_f32(acc, xs, ws)
+    ref64 = orc.epilogue_f64(acc, xs, ws)
+    xq_d = torch.from_numpy(xq).to(DEV)
+    packed = ops.prepack_weight(torch.from_numpy(wq).to(DEV))
+    xs_d, ws_d = torch.from_numpy(xs).to(DEV), torch.from_numpy(ws).to(DEV)
+    for t in range(ops.tile_count()):
+        got = ops.scaled_mm(xq_d, None, packed, None, N, out_dtype=torch.int32, tile=t)
+        assert np.array_equal(got.cpu().numpy(), acc), ops.tile_name(t)
+        out = ops.scaled_mm(xq_d, xs_d, packed, ws_d, N, tile=t)
+        assert check_out(bits_np(out), ref32, ref64, ops.tile_name(t)) == 1.0, ops.tile_name(t)
+
+
 def test_scaled_mm_strided_output_and_unaligned_rows(ops, orc):
     """Leading dimensions larger than the row, odd ldo (scalar store path)."""
     M, N, K = 70, 37, 96

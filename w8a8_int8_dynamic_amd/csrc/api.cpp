@@ -249,7 +249,7 @@ w8a8_status_t mm_args(const int8_t *xq, int64_t ldq, const float *x_scale, const
         return fail(W8A8_ERR_ALIGN, "%s: out must be aligned to its element size", what);
     if ((x_scale && !aligned(x_scale, 4)) || (!i32 && (!aligned(w_scale, 4) || (bias && !aligned(bias, 2)))))
         return fail(W8A8_ERR_ALIGN, "%s: scales/bias misaligned", what);
-    t = tile >= 0 ? tile : fp8 ? w8a8::mm_tile_auto_main(M, N, K) : w8a8::mm_tile_auto(M, N, K);
+    t = tile >= 0 ? tile : w8a8::mm_tile_auto(M, N, K);
     a.xq = xq;
     a.xs = (i32 && !need_xs) ? nullptr : x_scale;
     a.wp = reinterpret_cast<const int8_t *>(w_packed);
@@ -463,17 +463,18 @@ W8A8_API w8a8_status_t fp8_scaled_mm(const uint8_t *xq, int64_t ldq, const float
                               stream, -1);
 }
 
-W8A8_API w8a8_status_t fp8_quant_scaled_mm(const uint16_t *x, int64_t ldx, uint8_t *xq,
-                                           int64_t ldq, float *x_scale, const void *w_packed,
-                                           const float *w_scale, const uint16_t *bias, int64_t M,
-                                           int64_t N, int64_t K, int mode, void *out, int64_t ldo,
-                                           void *stream)
+W8A8_API w8a8_status_t fp8_quant_scaled_mm_tile(const uint16_t *x, int64_t ldx, uint8_t *xq,
+                                                int64_t ldq, float *x_scale, const void *w_packed,
+                                                const float *w_scale, const uint16_t *bias,
+                                                int64_t M, int64_t N, int64_t K, int mode,
+                                                void *out, int64_t ldo, void *stream, int tile)
 {
     const char *what = "fp8_quant_scaled_mm";
     w8a8::MmArgs a;
     int t;
     w8a8_status_t st = mm_args(reinterpret_cast<const int8_t *>(xq), ldq, x_scale, w_packed,
-                               w_scale, bias, M, N, K, mode, out, ldo, -1, true, what, a, t, true);
+                               w_scale, bias, M, N, K, mode, out, ldo, tile, true, what, a, t,
+                               true);
     if (st != W8A8_OK)
         return st;
     if (ldx < K)
@@ -488,6 +489,17 @@ W8A8_API w8a8_status_t fp8_quant_scaled_mm(const uint16_t *x, int64_t ldx, uint8
     if (st != W8A8_OK)
         return st;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // One launch where the int8 path would take one (the fused kernels read
+    // bf16 x for bf16 and raw output), else the two steps.
+    if (mode != W8A8_OUT_F16) {
+        a.x = x;
+        a.ldx = ldx;
+        hipError_t err = w8a8::launch_quant_scaled_mm_fp8(a, mode, t, s);
+        if (err != hipErrorNotSupported)
+            return launched(err, what);
+        (void)hipGetLastError();
+        a.x = nullptr;
+    }
     hipError_t err = w8a8::launch_quant_rows(x, w8a8::kElemBF16, M, K, ldx,
                                              reinterpret_cast<int8_t *>(xq), ldq, x_scale, s, true);
     if (err != hipSuccess)
@@ -495,11 +507,21 @@ W8A8_API w8a8_status_t fp8_quant_scaled_mm(const uint16_t *x, int64_t ldx, uint8
     return launched(w8a8::launch_scaled_mm_fp8(a, mode, t, s), what);
 }
 
+W8A8_API w8a8_status_t fp8_quant_scaled_mm(const uint16_t *x, int64_t ldx, uint8_t *xq,
+                                           int64_t ldq, float *x_scale, const void *w_packed,
+                                           const float *w_scale, const uint16_t *bias, int64_t M,
+                                           int64_t N, int64_t K, int mode, void *out, int64_t ldo,
+                                           void *stream)
+{
+    return fp8_quant_scaled_mm_tile(x, ldx, xq, ldq, x_scale, w_packed, w_scale, bias, M, N, K,
+                                    mode, out, ldo, stream, -1);
+}
+
 W8A8_API int w8a8_fp8_tile_count(void) { return w8a8::fp8_tile_count(); }
 
 W8A8_API int w8a8_fp8_tile_auto(int64_t M, int64_t N, int64_t K)
 {
-    return w8a8::mm_tile_auto_main(M, N, K);
+    return w8a8::mm_tile_auto(M, N, K);
 }
 
 W8A8_API int w8a8_mm_tile_count(void) { return w8a8::mm_tile_count(); }

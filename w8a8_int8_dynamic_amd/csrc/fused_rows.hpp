@@ -45,7 +45,7 @@ constexpr int kSpinLimit = 1 << 12;
 // per lane, 8 / CPL rows per wavefront in flight (all their loads issued
 // before the first reduction); the reduction stays inside the wavefront, so
 // there is no barrier. Wave w takes row groups w, w + NW, ... of [ra, rb).
-template <int THREADS, int CPL, int E>
+template <int THREADS, int CPL, int E, bool FP8>
 __device__ __forceinline__ void quantize_rows_by_wave(const MmArgs &a, int ra, int rb)
 {
     using namespace quant_rule;
@@ -74,14 +74,14 @@ __device__ __forceinline__ void quantize_rows_by_wave(const MmArgs &a, int ra, i
                 mx = max(mx, chunk_absmax<E>(v[i][c]));
             mx = wave_max(mx);
             float sc, inv;
-            scale_of(mx, E, sc, inv);
+            scale_of(mx, E, sc, inv, FP8);
             int8_t *qrow = const_cast<int8_t *>(a.xq) + (int64_t)(g + i) * a.ldq;
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 const int e = (c * 64 + lane) * 8;
                 if (e < a.K) {
                     u32 lo, hi;
-                    chunk_codes<E>(v[i][c], inv, lo, hi);
+                    chunk_codes<E, FP8>(v[i][c], inv, lo, hi);
                     __hip_atomic_store(reinterpret_cast<uint64_t *>(qrow + e), (uint64_t)hi << 32 | lo,
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
@@ -101,25 +101,25 @@ __device__ __forceinline__ void quantize_rows_by_wave(const MmArgs &a, int ra, i
 // registers (one read of x; two such rows at a time when they fit); longer
 // still take an absmax pass and a codes pass that re-reads the row from L2.
 // red: 2 * THREADS / 64 words of LDS. Every thread of the workgroup must
-// call this (it may hold barriers).
-template <int THREADS, int E>
+// call this (it may hold barriers). FP8: e4m3 codes and absmax / 448 scales.
+template <int THREADS, int E, bool FP8 = false>
 __device__ __forceinline__ void quantize_rows(const MmArgs &a, int ra, int rb, u32 *red)
 {
     using namespace quant_rule;
     if (a.K <= 64 * 8) {
-        quantize_rows_by_wave<THREADS, 1, E>(a, ra, rb);
+        quantize_rows_by_wave<THREADS, 1, E, FP8>(a, ra, rb);
         return;
     }
     if (a.K <= 64 * 8 * 2) {
-        quantize_rows_by_wave<THREADS, 2, E>(a, ra, rb);
+        quantize_rows_by_wave<THREADS, 2, E, FP8>(a, ra, rb);
         return;
     }
     if (a.K <= 64 * 8 * 4) {
-        quantize_rows_by_wave<THREADS, 4, E>(a, ra, rb);
+        quantize_rows_by_wave<THREADS, 4, E, FP8>(a, ra, rb);
         return;
     }
     if (a.K <= 64 * 8 * 8 && rb - ra > THREADS / 64) {
-        quantize_rows_by_wave<THREADS, 8, E>(a, ra, rb);
+        quantize_rows_by_wave<THREADS, 8, E, FP8>(a, ra, rb);
         return;
     }
     constexpr int NW = THREADS / 64;
@@ -172,14 +172,14 @@ __device__ __forceinline__ void quantize_rows(const MmArgs &a, int ra, int rb, u
 #pragma unroll
         for (int k = 0; k < NR; ++k) {
             float sc, inv;
-            scale_of(mx[k], E, sc, inv);
+            scale_of(mx[k], E, sc, inv, FP8);
             int8_t *qrow = const_cast<int8_t *>(a.xq) + (int64_t)(r + k) * a.ldq;
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
                 const int e = (c * THREADS + (int)threadIdx.x) * 8;
                 if (e < a.K) {
                     u32 lo, hi;
-                    chunk_codes<E>(v[k][c], inv, lo, hi);
+                    chunk_codes<E, FP8>(v[k][c], inv, lo, hi);
                     put_codes(qrow, e, lo, hi);
                 }
             }
@@ -201,10 +201,10 @@ __device__ __forceinline__ void quantize_rows(const MmArgs &a, int ra, int rb, u
             mx = max(mx, red[w]);
         __syncthreads();
         float sc, inv;
-        scale_of(mx, E, sc, inv);
+        scale_of(mx, E, sc, inv, FP8);
         for (int e = (int)threadIdx.x * 8; e < a.K; e += THREADS * 8) {
             u32 lo, hi;
-            chunk_codes<E>(load_chunk<E>(xrow, e, a.K), inv, lo, hi);
+            chunk_codes<E, FP8>(load_chunk<E>(xrow, e, a.K), inv, lo, hi);
             put_codes(qrow, e, lo, hi);
         }
         put_scale(r, sc);

@@ -78,6 +78,7 @@ struct TileEntry {
 // the tile numbering.
 int skinny_tile_count();
 const TileEntry &skinny_tile(int i);
+const TileEntry &skinny_tile_fp8(int i);     // the e4m3 twin's, same order
 // Fused quant + small-M matmul (each workgroup quantizes its own rows);
 // hipErrorNotSupported (nothing launched) when the rows are too long.
 hipError_t launch_skinny_quant_mm(const MmArgs &a, const TileEntry &e, int mode,
@@ -96,18 +97,22 @@ __device__ __forceinline__ int xcd_remap(int pid, int tiles)
 int mm_tile_count();
 const char *mm_tile_name(int tile);
 int mm_tile_auto(int64_t M, int64_t N, int64_t K);
-// The automatic choice among the main kernel's tiles only (numbers
-// 0 .. fp8_tile_count()-1, the tiles of the e4m3 twin).
-int mm_tile_auto_main(int64_t M, int64_t N, int64_t K);
 
 // ---- the e4m3 twin of the matmul (scaled_mm_fp8.hip) ----
-// mode kOutI32 stores the raw fp32 accumulators.
+// Tiles are numbered as the int8 ones (main, then small-M); mode kOutI32
+// stores the raw fp32 accumulators. The fused form returns
+// hipErrorNotSupported (nothing launched) as launch_quant_scaled_mm does.
 int fp8_tile_count();
 hipError_t launch_scaled_mm_fp8(const MmArgs &a, int mode, int tile, hipStream_t stream);
+hipError_t launch_quant_scaled_mm_fp8(MmArgs a, int mode, int tile, hipStream_t stream);
 hipError_t launch_scaled_mm(const MmArgs &a, int mode, int tile, hipStream_t stream);
 // Fused quant + matmul in one launch. Returns hipErrorNotSupported (nothing
 // launched) when the shape's workgroups cannot all be resident at once; the
 // caller then runs the two steps as separate launches.
 hipError_t launch_quant_scaled_mm(MmArgs a, int mode, int tile, hipStream_t stream);
+// The same for any tile entry; cap_key (< 32) names it in the per-device
+// cache of resident-workgroup capacities.
+hipError_t launch_quant_scaled_mm_entry(MmArgs a, int mode, const TileEntry &e, int cap_key,
+                                        hipStream_t stream);
 
 }  // namespace w8a8

@@ -199,11 +199,11 @@ struct Tile {
 // 16-bit type (bf16 for the int32 debug mode).
 // FP8: the e4m3 twin (operands are e4m3 codes in the same layout; one
 // v_mfma_scale_f32_32x32x64_f8f6f4 per k-block with unit block scales,
-// fp32 accumulators; kOutI32 then stores the raw fp32 accumulators).
+// fp32 accumulators; kOutI32 then stores the raw fp32 accumulators; the
+// fused form writes e4m3 codes).
 template <class T, int OUT, bool FUSED, bool FP8 = false>
 __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args)
 {
-    static_assert(!(FP8 && FUSED), "the e4m3 twin has no fused quant");
     constexpr bool OUT_I32 = OUT == kOutI32, OUT_F16 = OUT == kOutF16;
     using Acc = std::conditional_t<FP8, v16f, v16i>;
     constexpr int IN = OUT_F16 ? kElemF16 : kElemBF16;
@@ -432,12 +432,12 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
             reinterpret_cast<quant_rule::u32 *>(reinterpret_cast<char *>(lds) + T::FLAG);
         const int r0 = (int)blockIdx.x * a.rows_per_wg;
         const int r1 = min(r0 + a.rows_per_wg, a.M);
-        fused::quantize_rows<T::THREADS, IN>(a, r0, r1, red);
+        fused::quantize_rows<T::THREADS, IN, FP8>(a, r0, r1, red);
         fused::publish(a, r0 < r1);
         const int rows = min(T::BM, a.M - m0);
         const int producers = (rows + a.rows_per_wg - 1) / a.rows_per_wg;
         if (fused::wait_producers(a, m0 / a.rows_per_wg, producers, decision)) {
-            fused::quantize_rows<T::THREADS, IN>(a, m0, m0 + rows, red);
+            fused::quantize_rows<T::THREADS, IN, FP8>(a, m0, m0 + rows, red);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }

@@ -53,9 +53,7 @@ const char *mm_tile_name(int tile)
 //   whole weight), or the L2 reads of the workgroups if more: each k-block
 //   brings the weight fragments and one 128-byte line per token row, ~14
 //   TB/s in all; plus a fixed cost.
-namespace {
-
-int tile_auto(int64_t M, int64_t N, int64_t K, bool main_only)
+int mm_tile_auto(int64_t M, int64_t N, int64_t K)
 {
     const double cus = 256.0;
     const double kk = (double)round_up(K, 64), kblocks = kk / 64.0;
@@ -63,7 +61,7 @@ int tile_auto(int64_t M, int64_t N, int64_t K, bool main_only)
     double best_cost = 1e300;
     for (int t = 0; t < mm_tile_count(); ++t) {
         const TileEntry &e = tile_entry(t);
-        if (e.skinny && (main_only || M > 32))
+        if (e.skinny && M > 32)
             continue;
         const int64_t tiles_m = ceil_div(M, e.bm);
         const int64_t tiles = tiles_m * ceil_div(N, e.bn);
@@ -87,12 +85,6 @@ int tile_auto(int64_t M, int64_t N, int64_t K, bool main_only)
     }
     return best;
 }
-
-}  // namespace
-
-int mm_tile_auto(int64_t M, int64_t N, int64_t K) { return tile_auto(M, N, K, false); }
-
-int mm_tile_auto_main(int64_t M, int64_t N, int64_t K) { return tile_auto(M, N, K, true); }
 
 hipError_t launch_scaled_mm(const MmArgs &a, int mode, int tile, hipStream_t stream)
 {
@@ -130,7 +122,12 @@ static hipError_t fused_capacity(int dev, int tile, int mode, MmKernel fn, int t
 
 hipError_t launch_quant_scaled_mm(MmArgs a, int mode, int tile, hipStream_t stream)
 {
-    const TileEntry &e = tile_entry(tile);
+    return launch_quant_scaled_mm_entry(a, mode, tile_entry(tile), tile, stream);
+}
+
+hipError_t launch_quant_scaled_mm_entry(MmArgs a, int mode, const TileEntry &e, int cap_key,
+                                        hipStream_t stream)
+{
     const int64_t tiles = ceil_div(a.M, e.bm) * ceil_div(a.N, e.bn);
     MmKernel fn = e.fused[mode];
     if (fn == nullptr)
@@ -155,7 +152,7 @@ hipError_t launch_quant_scaled_mm(MmArgs a, int mode, int tile, hipStream_t stre
     // its own-rows fallback keeps an ordinary launch correct even where the
     // grid does not all run at once.)
     int cap = 0;
-    err = fused_capacity(dev, tile, mode, fn, e.threads, cap);
+    err = fused_capacity(dev, cap_key, mode, fn, e.threads, cap);
     if (err != hipSuccess)
         return err;
     if (tiles > cap)

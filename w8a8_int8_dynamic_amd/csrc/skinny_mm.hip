@@ -46,6 +46,8 @@ namespace w8a8 {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -74,7 +76,7 @@ struct Skinny {
 // rows are read once: thread t holds chunk c of row r (elements
 // (c*THREADS + t)*8 ..+8) in slot r*cpr + c, at most kQuantSlots of them.
 // Every thread calls this (it holds barriers).
-template <int THREADS, int E>
+template <int THREADS, int E, bool FP8>
 __device__ __forceinline__ void quantize_tile(const MmArgs &a, int m0, int rows, int pitch,
                                               bool writer, int8_t *tok, quant_rule::u32 *rowmax,
                                               float *rowscale)
@@ -110,10 +112,10 @@ __device__ __forceinline__ void quantize_tile(const MmArgs &a, int m0, int rows,
         if (s < slots) {
             const int r = s / cpr, e = ((s - r * cpr) * THREADS + (int)threadIdx.x) * 8;
             float sc, inv;
-            scale_of(rowmax[r], E, sc, inv);
+            scale_of(rowmax[r], E, sc, inv, FP8);
             if (e < a.K) {
                 u32 lo, hi;
-                chunk_codes<E>(v[s], inv, lo, hi);
+                chunk_codes<E, FP8>(v[s], inv, lo, hi);
                 *reinterpret_cast<v2u *>(tok + r * pitch + e) = v2u{lo, hi};
                 if (writer)
                     *reinterpret_cast<v2u *>(const_cast<int8_t *>(a.xq) + (int64_t)(m0 + r) * a.ldq + e) =
@@ -123,7 +125,7 @@ __device__ __forceinline__ void quantize_tile(const MmArgs &a, int m0, int rows,
     }
     if ((int)threadIdx.x < rows) {
         float sc, inv;
-        scale_of(rowmax[threadIdx.x], E, sc, inv);
+        scale_of(rowmax[threadIdx.x], E, sc, inv, FP8);
         rowscale[threadIdx.x] = sc;
         if (writer)
             const_cast<float *>(a.xs)[m0 + threadIdx.x] = sc;
@@ -133,9 +135,14 @@ __device__ __forceinline__ void quantize_tile(const MmArgs &a, int m0, int rows,
 
 // At least 16 wavefronts per CU (128 registers each): the kernel lives on
 // the loads it keeps in flight, so occupancy counts more than ILP.
-template <class S, int OUT, bool FUSED>
+// FP8: the e4m3 twin. Two k-blocks (the 1 KB fragments of k-blocks kb and
+// the next of this wave's) make one v_mfma_scale_f32_16x16x128_f8f6f4 on the
+// concatenated 16-byte halves of both operands (unit block scales), fp32
+// accumulators; a lone last k-block pairs with zero weights.
+template <class S, int OUT, bool FUSED, bool FP8 = false>
 __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kernel(const MmArgs a)
 {
+    using Acc = std::conditional_t<FP8, f32x4, v4i>;
     constexpr bool OUT_I32 = OUT == kOutI32, OUT_F16 = OUT == kOutF16;
     // The fused form reads x in the output's 16-bit type (bf16 for int32).
     constexpr int IN = OUT_F16 ? kElemF16 : kElemBF16;
@@ -173,12 +180,12 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
     }
     const int kc = 16 * (lane >> 4);
 
-    v4i acc[S::FM][S::FN];
+    Acc acc[S::FM][S::FN];
 #pragma unroll
     for (int f = 0; f < S::FM; ++f)
 #pragma unroll
         for (int j = 0; j < S::FN; ++j)
-            acc[f][j] = v4i{};
+            acc[f][j] = Acc{};
 
     auto wload = [&](int kb, v4i (&w)[S::FN]) __attribute__((always_inline)) {
 #pragma unroll
@@ -198,8 +205,44 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
 #pragma unroll
         for (int f = 0; f < S::FM; ++f)
 #pragma unroll
-            for (int j = 0; j < S::FN; ++j)
-                acc[f][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[j], x[f], acc[f][j], 0, 0, 0);
+            for (int j = 0; j < S::FN; ++j) {
+                if constexpr (!FP8)
+                    acc[f][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[j], x[f], acc[f][j], 0, 0, 0);
+            }
+    };
+    auto mma2 = [&](const v4i (&w0)[S::FN], const v4i (&x0)[S::FM], const v4i (&w1)[S::FN],
+                    const v4i (&x1)[S::FM]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int f = 0; f < S::FM; ++f)
+#pragma unroll
+            for (int j = 0; j < S::FN; ++j) {
+                if constexpr (FP8) {
+                    const v8i ww = __builtin_shufflevector(w0[j], w1[j], 0, 1, 2, 3, 4, 5, 6, 7);
+                    const v8i xx = __builtin_shufflevector(x0[f], x1[f], 0, 1, 2, 3, 4, 5, 6, 7);
+                    acc[f][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ww, xx, acc[f][j], 0, 0,
+                                                                               0, 127, 0, 127);
+                }
+            }
+    };
+    // The MFMAs of a load group's first n k-blocks (n is wave-uniform).
+    auto mma_group = [&](const v4i (&w)[S::U][S::FN], const v4i (&x)[S::U][S::FM], int n)
+                         __attribute__((always_inline)) {
+        if constexpr (FP8) {
+            static_assert(S::U % 2 == 0, "k-blocks go to the fp8 MFMA in pairs");
+            const v4i zero[S::FN] = {};
+#pragma unroll
+            for (int u = 0; u < S::U; u += 2) {
+                if (u + 1 < n)
+                    mma2(w[u], x[u], w[u + 1], x[u + 1]);
+                else if (u < n)
+                    mma2(w[u], x[u], zero, x[u]);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < S::U; ++u)
+                if (u < n)
+                    mma(w[u], x[u]);
+        }
     };
 
     // This wave's k-blocks: wk, wk+WK, ... (mine of them). Full load groups,
@@ -223,16 +266,14 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
 #pragma unroll
         for (int u = 0; u < S::U; ++u)
             wload(min(kb_of(u), KB - 1), w[u]);
-        quantize_tile<S::THREADS, IN>(a, m0, rows, pitch, nb0 == 0, tok, rowmax, rowscale);
+        quantize_tile<S::THREADS, IN, FP8>(a, m0, rows, pitch, nb0 == 0, tok, rowmax, rowscale);
         if (pre) {
             v4i x[S::U][S::FM];
 #pragma unroll
             for (int u = 0; u < S::U; ++u)
                 tload(kb_of(u), x[u]);
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int u = 0; u < S::U; ++u)
-                mma(w[u], x[u]);
+            mma_group(w, x, S::U);
             __builtin_amdgcn_sched_barrier(0);
             g = S::U;
         }
@@ -244,9 +285,7 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
         for (int u = 0; u < S::U; ++u)
             block(kb_of(g + u), w[u], x[u]);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < S::U; ++u)
-            mma(w[u], x[u]);
+        mma_group(w, x, S::U);
         __builtin_amdgcn_sched_barrier(0);
     }
     if (g < mine) {
@@ -256,10 +295,7 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
             if (g + u < mine)
                 block(kb_of(g + u), w[u], x[u]);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < S::U; ++u)
-            if (g + u < mine)
-                mma(w[u], x[u]);
+        mma_group(w, x, mine - g);
     }
 
     if (wk > 0) {
@@ -267,7 +303,7 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
         for (int f = 0; f < S::FM; ++f)
 #pragma unroll
             for (int j = 0; j < S::FN; ++j)
-                part[wk - 1][f * S::FN + j][lane] = acc[f][j];
+                part[wk - 1][f * S::FN + j][lane] = __builtin_bit_cast(v4i, acc[f][j]);
     }
     __syncthreads();
     if (wk != 0)
@@ -280,7 +316,7 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
         for (int f = 0; f < S::FM; ++f)
 #pragma unroll
             for (int j = 0; j < S::FN; ++j)
-                acc[f][j] += part[w][f * S::FN + j][lane];
+                acc[f][j] += __builtin_bit_cast(Acc, part[w][f * S::FN + j][lane]);
 
     const bool has_bias = !OUT_I32 && a.bias != nullptr;
 #pragma unroll
@@ -294,17 +330,17 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
             const int n = 16 * (nb0 + j) + 4 * (lane >> 4);
             if (n >= a.N)
                 continue;
-            const v4i c = acc[f][j];
+            const Acc c = acc[f][j];
             const bool whole = a.vec_store && n + 3 < a.N;
             if (OUT_I32) {
                 int *o = reinterpret_cast<int *>(a.out) + (int64_t)m * a.ldo + n;
                 if (whole) {
-                    *reinterpret_cast<v4i *>(o) = c;
+                    *reinterpret_cast<v4i *>(o) = __builtin_bit_cast(v4i, c);
                 } else {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         if (n + r < a.N)
-                            o[r] = c[r];
+                            o[r] = __builtin_bit_cast(v4i, c)[r];
                 }
                 continue;
             }
@@ -365,10 +401,33 @@ const TileEntry kSkinny[] = {
     skinny<Skinny<2, 1, 8, 4>>("s32x16/k8/u4"),
 };
 
+
+template <class S>
+constexpr TileEntry skinny_fp8(const char *name)
+{
+    return TileEntry{name, S::BM, S::BN, S::THREADS, true,
+                     {skinny_mm_kernel<S, kOutBF16, false, true>,
+                      skinny_mm_kernel<S, kOutI32, false, true>,
+                      skinny_mm_kernel<S, kOutF16, false, true>},
+                     {skinny_mm_kernel<S, kOutBF16, true, true>,
+                      skinny_mm_kernel<S, kOutI32, true, true>,
+                      skinny_mm_kernel<S, kOutF16, true, true>}};
+}
+
+// The e4m3 twin's small-M configurations, in the same order.
+const TileEntry kSkinnyFp8[] = {
+    skinny_fp8<Skinny<1, 1, 8, 4>>("s16x16/k8/u4"),
+    skinny_fp8<Skinny<1, 1, 4, 4>>("s16x16/k4/u4"),
+    skinny_fp8<Skinny<1, 2, 8, 4>>("s16x32/k8/u4"),
+    skinny_fp8<Skinny<2, 1, 8, 4>>("s32x16/k8/u4"),
+};
+static_assert(sizeof(kSkinnyFp8) == sizeof(kSkinny), "the twin has the same configurations");
+
 }  // namespace
 
 int skinny_tile_count() { return (int)(sizeof(kSkinny) / sizeof(kSkinny[0])); }
 const TileEntry &skinny_tile(int i) { return kSkinny[i]; }
+const TileEntry &skinny_tile_fp8(int i) { return kSkinnyFp8[i]; }
 
 hipError_t launch_skinny_quant_mm(const MmArgs &a, const TileEntry &e, int mode,
                                   hipStream_t stream)

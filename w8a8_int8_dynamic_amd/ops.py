@@ -325,27 +325,33 @@ def fp8_scaled_mm(xq: torch.Tensor, xs: Optional[torch.Tensor], w_packed: torch.
     return out
 
 
-def fp8_quant_scaled_mm(x: torch.Tensor, w_packed: torch.Tensor, ws: torch.Tensor, N: int,
-                        bias: Optional[torch.Tensor] = None,
+def fp8_quant_scaled_mm(x: torch.Tensor, w_packed: torch.Tensor, ws: Optional[torch.Tensor],
+                        N: int, bias: Optional[torch.Tensor] = None,
                         out_dtype: torch.dtype = torch.bfloat16,
-                        out: Optional[torch.Tensor] = None
+                        out: Optional[torch.Tensor] = None, tile: int = -1
                         ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """e4m3 per-token quant of bf16 x and the e4m3 scaled matmul: (out, xq, xs)."""
+    """e4m3 per-token quant of bf16 x and the e4m3 scaled matmul: (out, xq, xs).
+    out_dtype bf16 or fp16, or float32 for the raw fp32 accumulators."""
     _matrix(x, "x", torch.bfloat16)
     M, K = x.shape
     x = _rows_aligned(x, 8)
-    if out_dtype not in (torch.bfloat16, torch.float16):
-        raise TypeError("out_dtype must be torch.bfloat16 or torch.float16")
-    _vector(ws, N, "ws", torch.float32)
-    _vector(bias, N, "bias", out_dtype)
+    if out_dtype not in _FP8_OUT_MODE:
+        raise TypeError("out_dtype must be torch.bfloat16, torch.float16 or torch.float32")
+    mode = _FP8_OUT_MODE[out_dtype]
+    if mode != W8A8_OUT_I32:
+        _vector(ws, N, "ws", torch.float32)
+        _vector(bias, N, "bias", out_dtype)
     xq = _fp8_codes(M, K, x.device)
     xs = torch.empty((M,), dtype=torch.float32, device=x.device)
     out = torch.empty((M, N), dtype=out_dtype, device=x.device) if out is None else out
     _matrix(out, "out", out_dtype)
+    def ptr(t):
+        return None if t is None or mode == W8A8_OUT_I32 else t.data_ptr()
+
     with torch.cuda.device(x.device):
-        call("fp8_quant_scaled_mm", x.data_ptr(), _ld(x), xq.data_ptr(), _ld(xq), xs.data_ptr(),
-             w_packed.data_ptr(), ws.data_ptr(), None if bias is None else bias.data_ptr(), M, N,
-             K, _FP8_OUT_MODE[out_dtype], out.data_ptr(), _ld(out), _stream(x))
+        call("fp8_quant_scaled_mm_tile", x.data_ptr(), _ld(x), xq.data_ptr(), _ld(xq),
+             xs.data_ptr(), w_packed.data_ptr(), ptr(ws), ptr(bias), M, N, K, mode,
+             out.data_ptr(), _ld(out), _stream(x), tile)
     return out, xq, xs
 
 
