@@ -225,9 +225,19 @@ w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const float *x_
  * its own tile's rows; should a wait ever run out, that workgroup quantizes
  * its tile's rows itself, so the result never depends on scheduling. Calls
  * that overlap on one device therefore stay correct (each sees only its own
- * launch's flags) but may take that slower path. Otherwise (the small-M
- * tiles, or a grid too large to be resident) the two steps run as two
- * launches on `stream`.
+ * launch's flags) but may take that slower path. The launch number is
+ * fixed when the launch is made, so a call made while `stream` is being
+ * captured into a graph takes the two launches instead (a replayed graph
+ * would otherwise reuse one number).
+ *
+ * With a small-M tile and at most two token rows (K up to 4096 for two
+ * rows, 8192 for one), one launch also does both steps, with no flags: each
+ * workgroup quantizes the rows into its own LDS and the workgroups of the
+ * first column block also write xq and x_scale. This form is safe under
+ * graph capture.
+ *
+ * Otherwise (a grid too large to be resident, or more rows on a small-M
+ * tile) the two steps run as two launches on `stream`.
  */
 w8a8_status_t int8_quant_scaled_mm(const uint16_t *x, int64_t ldx, int8_t *xq, int64_t ldq,
                                    float *x_scale, const void *w_packed, const float *w_scale,

@@ -105,8 +105,9 @@ def test_fp8_quant_per_token_workload(ops, orc, name):
 
 
 def test_fp8_quant_edges(ops, orc):
-    """Rows built to land x*inv on e4m3 ties, subnormal codes, signed zeros
-    and the 448 edge; ragged K; the two-pass kernel (K = 40000)."""
+    """Rows built to land x*inv on e4m3 ties, subnormal codes, signed zeros,
+    fp32-subnormal products and the 448 edge; ragged K; the two-pass kernel
+    (K = 40000)."""
     rng = np.random.default_rng(8100)
     rows = []
     # absmax 448 -> inv = 1: the row's values are scaled codes directly
@@ -117,6 +118,10 @@ def test_fp8_quant_edges(ops, orc):
     rows.append(np.resize(-ties, 50))
     rows.append(np.zeros(50, np.float32))
     rows.append((rng.standard_normal(50) * 1e-3).astype(np.float32))
+    # absmax near the bf16 maximum: small entries give fp32-subnormal x*inv
+    # (codes +-0, sign kept) next to ordinary codes
+    rows.append(np.resize(np.array([3e38, -1e-3, 1e-3, -1e-36, 2e-36, -3e35, 1e35, 0.0],
+                                   np.float32), 50))
     x = wl.f32_to_bf16_bits(np.stack(rows))
     for arr in (x, wl.f32_to_bf16_bits((rng.standard_normal((7, 40000)) * 3).astype(np.float32)),
                 wl.f32_to_bf16_bits((rng.standard_normal((65, 200)) * 10).astype(np.float32))):
@@ -222,6 +227,51 @@ def test_fp8_quant_scaled_mm_every_tile(ops, orc, M, N, K):
             torch.cuda.synchronize()
             assert np.array_equal(xq.cpu().numpy(), xq_ref), name
             assert np.array_equal(bits_np(out), own32), name
+
+
+def test_fp8_quant_scaled_mm_graph_replays_new_inputs(ops, orc):
+    """The main-tile fp8_quant_scaled_mm captured in a HIP graph and replayed
+    with a different input copied into the captured x before each replay:
+    codes and scales bit-exact to the oracle for the input of that replay;
+    raw accumulators within the bound; bf16 outputs bit-exact to the
+    epilogue on those accumulators."""
+    M, N, K = 512, 1536, 512
+    inps = [wl.random_case(M, K, N, 8600 + i, bias=True) for i in range(2)]
+    wq, ws_ref = orc.fp8_quant_per_channel(inps[0].w_f32)
+    packed, ws = ops.fp8_quant_prepack_weight(torch.from_numpy(inps[0].w_f32).to(DEV))
+    b = bf16_dev(inps[0].bias_bf16)
+    refs = []
+    for inp in inps:
+        xq_ref, xs_ref = orc.fp8_quant_per_token(inp.x_bf16)
+        xq_dev = torch.from_numpy(xq_ref.view(np.uint8)).to(DEV)
+        acc = ops.fp8_scaled_mm(xq_dev, None, packed, None, N, out_dtype=torch.float32)
+        acc = acc.cpu().numpy()
+        check_acc(orc, acc, xq_ref, wq, orc.fp8_gemm(xq_ref, wq), "graph case")
+        own32, _ = orc.fp8_epilogue(acc.astype(np.float64), xs_ref, ws_ref, inps[0].bias_bf16)
+        refs.append((xq_ref, xs_ref, own32))
+    xs_dev = [bf16_dev(inp.x_bf16) for inp in inps]
+    x = xs_dev[0].clone()
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ops.fp8_quant_scaled_mm(x, packed, ws, N, b, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _, xq, xs = ops.fp8_quant_scaled_mm(x, packed, ws, N, b, out=out)
+    for i in range(6):
+        c = i % 2
+        x.copy_(xs_dev[c])
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        xq_ref, xs_ref, own32 = refs[c]
+        assert np.array_equal(xs.cpu().numpy(), xs_ref), f"replay {i}"
+        assert np.array_equal(xq.cpu().numpy(), xq_ref), f"replay {i}"
+        assert np.array_equal(bits_np(out), own32), f"replay {i}"
+        ops.fp8_quant_scaled_mm(xs_dev[1 - c], packed, ws, N, b)   # eager call between
 
 
 def test_fp8_full_size_fused_qkv(ops, orc):

@@ -450,6 +450,55 @@ def test_quant_scaled_mm_decode_graph_replays(ops, orc, M):
         ops.scaled_mm(xq, xs, packed, ws, N, b)    # eager work between replays
 
 
+def test_quant_scaled_mm_main_graph_replays_new_inputs(ops, orc):
+    """A main-tile call (eagerly the one-launch path with producer flags)
+    captured in a HIP graph, replayed with a different input copied into
+    the captured x before each replay. Each replay must match the oracle
+    for the input it saw: a replay must never take an earlier replay's
+    quantized rows."""
+    M, N, K = 512, 1536, 512
+    cases = []
+    for i in range(2):
+        inp = wl.random_case(M, K, N, 9400 + i, bias=True)
+        xq_ref, xs_ref = orc.quant_per_token(inp.x_bf16)
+        cases.append((inp, xq_ref, xs_ref))
+    w_inp = cases[0][0]
+    wq_ref, ws_ref = orc.quant_per_channel(w_inp.w_f32)
+    packed = ops.prepack_weight(torch.from_numpy(wq_ref).to(DEV))
+    ws, b = torch.from_numpy(ws_ref).to(DEV), bf16_dev(w_inp.bias_bf16)
+    refs = []
+    for inp, xq_ref, xs_ref in cases:
+        acc = orc.gemm_i32(xq_ref, wq_ref)
+        refs.append((orc.epilogue_f32(acc, xs_ref, ws_ref, w_inp.bias_bf16),
+                     orc.epilogue_f64(acc, xs_ref, ws_ref, w_inp.bias_bf16)))
+    xs_dev = [bf16_dev(inp.x_bf16) for inp, _, _ in cases]
+    x = xs_dev[0].clone()
+    xq = torch.empty((M, K), dtype=torch.int8, device=DEV)
+    xs = torch.empty((M,), dtype=torch.float32, device=DEV)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ops.quant_scaled_mm(x, packed, ws, N, b, out=out, xq=xq, xs=xs)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ops.quant_scaled_mm(x, packed, ws, N, b, out=out, xq=xq, xs=xs)
+    for i in range(6):
+        c = i % 2
+        x.copy_(xs_dev[c])
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _, xq_ref, xs_ref = cases[c]
+        assert np.array_equal(xs.cpu().numpy(), xs_ref), f"replay {i}"
+        assert np.array_equal(xq.cpu().numpy(), xq_ref), f"replay {i}"
+        exact = check_out(bits_np(out), refs[c][0], refs[c][1], f"replay {i}")
+        assert exact == 1.0, f"replay {i}"
+        ops.quant_scaled_mm(xs_dev[1 - c], packed, ws, N, b)    # eager one-launch call between
+
+
 def test_quant_scaled_mm_alternating_shapes(ops, orc):
     """Calls of different shapes back to back on one stream, each checked."""
     cases = []

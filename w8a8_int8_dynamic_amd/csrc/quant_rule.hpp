@@ -78,26 +78,30 @@ __device__ __forceinline__ u32 code(float f, float inv)
     return (u32)((int)t) & 0xffu;
 }
 
-// The e4m3 twin's code (OCP e4m3: 4 exponent bits, bias 7, 3 mantissa
-// bits, largest finite 448): t = clamp(fl32(f*inv), -448, 448) rounded to
-// the nearest e4m3 value, ties to even, the sign kept (zeros included).
-// From 2^-6 up the fp32 pattern is rounded to 3 mantissa bits (a carry
-// moves into the exponent) and rebiased; below, the step is 2^-9 and the
-// code is rint(|t| * 2^9).
-__device__ __forceinline__ u32 code_fp8(float f, float inv)
+// The e4m3 twin's codes of four values (OCP e4m3: 4 exponent bits, bias 7,
+// 3 mantissa bits, largest finite 448): t = clamp(fl32(f*inv), -448, 448)
+// rounded to the nearest e4m3 value, ties to even, the sign kept (zeros
+// included). gfx950's packed fp32 -> e4m3 conversion does the rounding, two
+// values per instruction (bytes 0-1, then 2-3); the clamp keeps every input
+// inside the finite range, away from its overflow handling.
+__device__ __forceinline__ u32 codes4_fp8(float f0, float f1, float f2, float f3, float inv)
 {
-    const float t = fminf(fmaxf(f * inv, -448.0f), 448.0f);
-    const u32 u = __float_as_uint(t);
-    const u32 a = u & 0x7fffffffu;
-    const u32 mag = a < 0x3c800000u ? (u32)__builtin_rintf(__uint_as_float(a) * 512.0f)
-                                    : ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-    return (u >> 24 & 0x80u) | mag;
+    auto t = [inv](float f) __attribute__((always_inline)) {
+        return fminf(fmaxf(f * inv, -448.0f), 448.0f);
+    };
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(t(f0), t(f1), 0, false);
+    return (u32)__builtin_amdgcn_cvt_pk_fp8_f32(t(f2), t(f3), lo, true);
+}
+
+__device__ __forceinline__ u32 codes4_i8(float f0, float f1, float f2, float f3, float inv)
+{
+    return code(f0, inv) | code(f1, inv) << 8 | code(f2, inv) << 16 | code(f3, inv) << 24;
 }
 
 template <bool FP8>
-__device__ __forceinline__ u32 code_of(float f, float inv)
+__device__ __forceinline__ u32 codes4(float f0, float f1, float f2, float f3, float inv)
 {
-    return FP8 ? code_fp8(f, inv) : code(f, inv);
+    return FP8 ? codes4_fp8(f0, f1, f2, f3, inv) : codes4_i8(f0, f1, f2, f3, inv);
 }
 
 // Codes of one chunk: bf16 or fp16 -> 8 codes in (lo, hi); fp32 -> 4 codes
@@ -107,24 +111,23 @@ __device__ __forceinline__ void chunk_codes(const uint4 &v, float inv, u32 &lo, 
 {
     const u32 d[4] = {v.x, v.y, v.z, v.w};
     if (E == kF32) {
-        lo = code_of<FP8>(__uint_as_float(d[0]), inv) | code_of<FP8>(__uint_as_float(d[1]), inv) << 8 |
-             code_of<FP8>(__uint_as_float(d[2]), inv) << 16 |
-             code_of<FP8>(__uint_as_float(d[3]), inv) << 24;
+        lo = codes4<FP8>(__uint_as_float(d[0]), __uint_as_float(d[1]), __uint_as_float(d[2]),
+                         __uint_as_float(d[3]), inv);
         hi = 0;
     } else {
-        u32 c[8];
+        float f[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (E == kF16) {
-                c[2 * i] = code_of<FP8>(f16_to_float(d[i]), inv);
-                c[2 * i + 1] = code_of<FP8>(f16_to_float(d[i] >> 16), inv);
+                f[2 * i] = f16_to_float(d[i]);
+                f[2 * i + 1] = f16_to_float(d[i] >> 16);
             } else {
-                c[2 * i] = code_of<FP8>(__uint_as_float(d[i] << 16), inv);
-                c[2 * i + 1] = code_of<FP8>(__uint_as_float(d[i] & 0xffff0000u), inv);
+                f[2 * i] = __uint_as_float(d[i] << 16);
+                f[2 * i + 1] = __uint_as_float(d[i] & 0xffff0000u);
             }
         }
-        lo = c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24;
-        hi = c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24;
+        lo = codes4<FP8>(f[0], f[1], f[2], f[3], inv);
+        hi = codes4<FP8>(f[4], f[5], f[6], f[7], inv);
     }
 }
 

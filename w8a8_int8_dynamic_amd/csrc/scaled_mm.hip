@@ -141,8 +141,18 @@ hipError_t launch_quant_scaled_mm_entry(MmArgs a, int mode, const TileEntry &e, 
         rpw *= 2;
     if (e.bm % rpw != 0 || ceil_div(a.M, rpw) > fused::kMaxProducers)
         return hipErrorNotSupported;
+    // The flags carry an epoch fixed when the launch is made. A captured graph
+    // would replay one epoch forever, and a replay could then take the flags
+    // its predecessor raised for its own rows; so under stream capture the
+    // caller runs the two launches instead.
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    hipError_t err = hipStreamIsCapturing(stream, &capture);
+    if (err != hipSuccess)
+        return err;
+    if (capture != hipStreamCaptureStatusNone)
+        return hipErrorNotSupported;
     int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
+    err = hipGetDevice(&dev);
     if (err != hipSuccess)
         return err;
     // Every workgroup waits for rows that other workgroups produce, so the
