@@ -185,6 +185,10 @@ w8a8_status_t int8_unpack_weight(const void *w_packed, int64_t N, int64_t K, int
  * with K a multiple of 16, ldq >= K, ldo >= N; xq and w_packed 16-byte
  * aligned, ldq a multiple of 16; out aligned to its element size. In I32
  * mode x_scale, w_scale and bias may be NULL and are ignored.
+ * Errors: W8A8_ERR_SHAPE also when the tile's workgroups over M x N, times
+ * its threads, do not fit in 32 bits (one launch's grid). That takes more
+ * than about 2^36 outputs on the smallest main tile, or more than about 2^27
+ * channels on a small-M tile.
  */
 w8a8_status_t int8_scaled_mm(const int8_t *xq, int64_t ldq, const float *x_scale,
                              const void *w_packed, const float *w_scale, const uint16_t *bias,

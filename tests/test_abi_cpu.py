@@ -171,6 +171,12 @@ def test_scaled_mm_validation():
     assert mm(xs=A + 2) == ALIGN and mm(bias=A + 1) == ALIGN
     # int32 debug mode ignores scales and bias
     assert mm(mode=1, xs=None, ws=None, bias=A + 1) in (OK, DEVICE)
+    # a grid whose workgroups times threads cannot fit one launch is refused
+    # on the host, for the forced smallest tile and for the automatic one
+    big = 2 ** 31 - 1
+    assert mm(M=big, N=big, ldo=big, tile=0) == SHAPE
+    assert mm(M=big, N=big, ldo=big) == SHAPE
+    assert mm(M=2 ** 24, N=16, tile=0) in (OK, DEVICE)     # 2^18 workgroups fit
 
 
 def qmm(x=A, ldx=64, xq=A, ldq=64, xs=A, wp=A, ws=A, bias=None, M=4, N=16, K=64, mode=0, out=A,
@@ -194,6 +200,54 @@ def test_quant_scaled_mm_validation():
     assert qmm(M=0, x=None, xq=None, xs=None, wp=None, ws=None, out=None) == OK
 
 
+def fp8_mm(xq=A, ldq=64, xs=A, wp=A, ws=A, bias=None, M=4, N=16, K=64, mode=0, out=A, ldo=16,
+           tile=-1):
+    return L.fp8_scaled_mm_tile(xq, ldq, xs, wp, ws, bias, M, N, K, mode, out, ldo, None, tile)
+
+
+def fp8_qmm(x=A, ldx=64, xq=A, ldq=64, xs=A, wp=A, ws=A, bias=None, M=4, N=16, K=64, mode=0,
+            out=A, ldo=16, tile=-1):
+    return L.fp8_quant_scaled_mm_tile(x, ldx, xq, ldq, xs, wp, ws, bias, M, N, K, mode, out, ldo,
+                                      None, tile)
+
+
+def test_fp8_entry_points_validation():
+    """The e4m3 twin's entry points apply the int8 rules on the host."""
+    assert L.w8a8_fp8_tile_count() == L.w8a8_mm_tile_count()
+    for shape in [(512, 12288, 4096), (1, 12288, 4096), (8, 3072, 12288)]:
+        assert L.w8a8_fp8_tile_auto(*shape) == L.w8a8_mm_tile_auto(*shape)
+    # quant
+    fq = lambda **k: L.fp8_quant_per_token(k.get("x", A), k.get("M", 4), k.get("K", 64),
+                                           k.get("ldx", 64), k.get("q", A), k.get("ldq", 64),
+                                           k.get("s", A), None)
+    assert fq(M=-1) == SHAPE and fq(K=0) == SHAPE and fq(ldx=32) == SHAPE and fq(ldq=32) == SHAPE
+    assert fq(x=None) == NULL and fq(q=None) == NULL and fq(s=None) == NULL
+    assert fq(x=A + 8) == ALIGN and fq(ldx=68) == ALIGN and fq(q=A + 4) == ALIGN
+    assert fq(M=0, x=None, q=None, s=None) == OK
+    fc = lambda **k: L.fp8_quant_per_channel(k.get("w", A), k.get("N", 4), k.get("K", 64),
+                                             k.get("ldw", 64), k.get("q", A), k.get("ldq", 64),
+                                             k.get("s", A), None)
+    assert fc(ldw=32) == SHAPE and fc(w=None) == NULL and fc(w=A + 8) == ALIGN and fc(ldw=66) == ALIGN
+    # online weight quant
+    fp = lambda **k: L.fp8_quant_prepack_weight(k.get("w", A), k.get("dt", 1), k.get("N", 16),
+                                                k.get("K", 64), k.get("ldw", 64), k.get("p", A),
+                                                k.get("s", A), None)
+    assert fp(dt=7) == MODE and fp(N=0) == SHAPE and fp(ldw=32) == SHAPE
+    assert fp(w=None) == NULL and fp(s=None) == NULL and fp(p=A + 8) == ALIGN
+    # matmul
+    assert fp8_mm(mode=3) == MODE and fp8_mm(tile=L.w8a8_fp8_tile_count()) == MODE
+    assert fp8_mm(K=72) == SHAPE and fp8_mm(ldq=48) == SHAPE and fp8_mm(ldo=15) == SHAPE
+    assert fp8_mm(xq=None) == NULL and fp8_mm(ws=None) == NULL and fp8_mm(xs=None) == NULL
+    assert fp8_mm(xq=A + 8) == ALIGN and fp8_mm(out=A + 1) == ALIGN
+    assert fp8_mm(M=0, xq=None, xs=None, wp=None, ws=None, out=None) == OK
+    big = 2 ** 31 - 1
+    assert fp8_mm(M=big, N=big, ldo=big, tile=0) == SHAPE
+    # fused
+    assert fp8_qmm(ldx=48) == SHAPE and fp8_qmm(x=None) == NULL and fp8_qmm(x=A + 8) == ALIGN
+    assert fp8_qmm(mode=1, xs=None, ws=None) == NULL
+    assert fp8_qmm(M=0, x=None, xq=None, xs=None, wp=None, ws=None, out=None) == OK
+
+
 def test_no_fallback_without_device():
     import torch
     if torch.cuda.is_available():
@@ -202,6 +256,8 @@ def test_no_fallback_without_device():
     assert mm() == DEVICE
     assert qmm() == DEVICE
     assert L.int8_prepack_weight(A, 16, 64, 64, A, None) == DEVICE
+    assert fp8_mm() == DEVICE and fp8_qmm() == DEVICE
+    assert L.fp8_quant_per_token(A, 4, 64, 64, A, 64, A, None) == DEVICE
     assert L.w8a8_device_supported(0) == 0
     assert "device" in _lib.last_error()
 

@@ -250,6 +250,9 @@ w8a8_status_t mm_args(const int8_t *xq, int64_t ldq, const float *x_scale, const
     if ((x_scale && !aligned(x_scale, 4)) || (!i32 && (!aligned(w_scale, 4) || (bias && !aligned(bias, 2)))))
         return fail(W8A8_ERR_ALIGN, "%s: scales/bias misaligned", what);
     t = tile >= 0 ? tile : w8a8::mm_tile_auto(M, N, K);
+    if (!(fp8 ? w8a8::fp8_launch_fits(t, M, N) : w8a8::mm_launch_fits(t, M, N)))
+        return fail(W8A8_ERR_SHAPE, "%s: M x N needs more workgroups of tile %d than one launch holds",
+                    what, t);
     a.xq = xq;
     a.xs = (i32 && !need_xs) ? nullptr : x_scale;
     a.wp = reinterpret_cast<const int8_t *>(w_packed);

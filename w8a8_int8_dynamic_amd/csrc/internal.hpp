@@ -15,6 +15,17 @@ constexpr int kFragBytes = 1024;
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
+// A launch's workgroups times threads per workgroup must fit in 32 bits.
+// Launchers whose grid grows with the data split it into launches of at
+// most this many workgroups (2^30 threads at 256 per workgroup); the matmul
+// launchers, whose grid is fixed by the tile, report a grid that cannot fit
+// (mm_grid_fits).
+constexpr int64_t kMaxBlocksPerLaunch = int64_t(1) << 22;
+inline bool mm_grid_fits(int64_t workgroups, int threads)
+{
+    return workgroups <= INT32_MAX && workgroups * threads <= (int64_t)UINT32_MAX;
+}
+
 // Element kinds of rows and outputs (the quant rule's kBF16 / kF32 / kF16).
 constexpr int kElemBF16 = 0, kElemF32 = 1, kElemF16 = 2;
 
@@ -97,6 +108,10 @@ __device__ __forceinline__ int xcd_remap(int pid, int tiles)
 int mm_tile_count();
 const char *mm_tile_name(int tile);
 int mm_tile_auto(int64_t M, int64_t N, int64_t K);
+// Whether the grid of tile `tile` over an M x N output fits one launch
+// (mm_grid_fits); fp8_launch_fits is the same for the e4m3 twin's tiles.
+bool mm_launch_fits(int tile, int64_t M, int64_t N);
+bool fp8_launch_fits(int tile, int64_t M, int64_t N);
 
 // ---- the e4m3 twin of the matmul (scaled_mm_fp8.hip) ----
 // Tiles are numbered as the int8 ones (main, then small-M); mode kOutI32

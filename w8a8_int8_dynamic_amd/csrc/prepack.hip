@@ -15,6 +15,8 @@
 // of quant.hip applied to a bf16 or fp32 weight and written straight into
 // the fragment layout above, so the int8 weight never exists unpacked (or,
 // for the e4m3 twin, the same with e4m3 codes and scale absmax / 448).
+#include <algorithm>
+
 #include "internal.hpp"
 #include "quant_rule.hpp"
 
@@ -23,9 +25,9 @@ namespace {
 
 __global__ __launch_bounds__(256) void prepack_kernel(const int8_t *__restrict__ wq, int N, int K,
                                                       int64_t ldw, uint4 *__restrict__ packed,
-                                                      int64_t units, int kblocks)
+                                                      int64_t units, int kblocks, int64_t u0)
 {
-    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t u = u0 + (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (u >= units)
         return;
     const int lane = (int)(u & 63);
@@ -46,9 +48,9 @@ __global__ __launch_bounds__(256) void prepack_kernel(const int8_t *__restrict__
 
 __global__ __launch_bounds__(256) void unpack_kernel(const uint4 *__restrict__ packed, int N, int K,
                                                      int8_t *__restrict__ wq, int64_t ldw,
-                                                     int64_t units, int kblocks)
+                                                     int64_t units, int kblocks, int64_t u0)
 {
-    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t u = u0 + (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (u >= units)
         return;
     const int lane = (int)(u & 63);
@@ -77,12 +79,13 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint4 *__restrict__ p
 template <bool F32, bool FP8>
 __global__ __launch_bounds__(256) void quant_prepack_kernel(const char *__restrict__ w, int N, int K,
                                                             int64_t ldw, uint4 *__restrict__ packed,
-                                                            float *__restrict__ w_scale, int kblocks)
+                                                            float *__restrict__ w_scale, int kblocks,
+                                                            int nb0)
 {
     using namespace quant_rule;
     constexpr int VEC = Elem<F32>::VEC, B = Elem<F32>::BYTES;
     __shared__ u32 rowmax[16];
-    const int nb = blockIdx.x;
+    const int nb = nb0 + (int)blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -134,11 +137,20 @@ hipError_t launch_quant_prepack(const void *w, bool w_f32, int64_t N, int64_t K,
 {
     const int64_t kblocks = ceil_div(K, kFragK);
     const int64_t nblocks = ceil_div(N, kFragN);
-    hipLaunchKernelGGL(w_f32 ? (fp8 ? quant_prepack_kernel<true, true> : quant_prepack_kernel<true, false>)
-                             : (fp8 ? quant_prepack_kernel<false, true> : quant_prepack_kernel<false, false>),
-                       dim3((unsigned)nblocks), dim3(256), 0, stream, reinterpret_cast<const char *>(w),
-                       (int)N, (int)K, ldw, reinterpret_cast<uint4 *>(packed), w_scale, (int)kblocks);
-    return hipGetLastError();
+    auto fn = w_f32 ? (fp8 ? quant_prepack_kernel<true, true> : quant_prepack_kernel<true, false>)
+                    : (fp8 ? quant_prepack_kernel<false, true> : quant_prepack_kernel<false, false>);
+    // A launch's workgroups times threads must fit in 32 bits: large
+    // weights go in slices of fragment rows.
+    for (int64_t nb0 = 0; nb0 < nblocks; nb0 += kMaxBlocksPerLaunch) {
+        const int64_t blocks = std::min(nblocks - nb0, kMaxBlocksPerLaunch);
+        hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           reinterpret_cast<const char *>(w), (int)N, (int)K, ldw,
+                           reinterpret_cast<uint4 *>(packed), w_scale, (int)kblocks, (int)nb0);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_prepack(const int8_t *wq, int64_t N, int64_t K, int64_t ldw, void *packed,
@@ -146,10 +158,15 @@ hipError_t launch_prepack(const int8_t *wq, int64_t N, int64_t K, int64_t ldw, v
 {
     const int64_t kblocks = ceil_div(K, kFragK);
     const int64_t units = ceil_div(N, kFragN) * kblocks * 64;
-    hipLaunchKernelGGL(prepack_kernel, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0, stream,
-                       wq, (int)N, (int)K, ldw, reinterpret_cast<uint4 *>(packed), units,
-                       (int)kblocks);
-    return hipGetLastError();
+    for (int64_t u0 = 0; u0 < units; u0 += kMaxBlocksPerLaunch * 256) {
+        const int64_t blocks = std::min(ceil_div(units - u0, 256), kMaxBlocksPerLaunch);
+        hipLaunchKernelGGL(prepack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, wq, (int)N,
+                           (int)K, ldw, reinterpret_cast<uint4 *>(packed), units, (int)kblocks, u0);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_unpack(const void *packed, int64_t N, int64_t K, int8_t *wq, int64_t ldw,
@@ -157,10 +174,16 @@ hipError_t launch_unpack(const void *packed, int64_t N, int64_t K, int8_t *wq, i
 {
     const int64_t kblocks = ceil_div(K, kFragK);
     const int64_t units = ceil_div(N, kFragN) * kblocks * 64;
-    hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0, stream,
-                       reinterpret_cast<const uint4 *>(packed), (int)N, (int)K, wq, ldw, units,
-                       (int)kblocks);
-    return hipGetLastError();
+    for (int64_t u0 = 0; u0 < units; u0 += kMaxBlocksPerLaunch * 256) {
+        const int64_t blocks = std::min(ceil_div(units - u0, 256), kMaxBlocksPerLaunch);
+        hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           reinterpret_cast<const uint4 *>(packed), (int)N, (int)K, wq, ldw, units,
+                           (int)kblocks, u0);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+    }
+    return hipSuccess;
 }
 
 }  // namespace w8a8

@@ -30,6 +30,8 @@
 //     that re-reads the row (from L2) for the quantize pass.
 // Every tail (K not a multiple of the chunk width, rows beyond the last)
 // is masked element by element.
+#include <algorithm>
+
 #include "internal.hpp"
 #include "quant_rule.hpp"
 
@@ -162,12 +164,36 @@ QuantFn pick(int wpr, int ch_idx)
 
 }  // namespace
 
+namespace {
+
+// Launches fn over rows [0, rows) in slices of at most kMaxBlocksPerLaunch
+// workgroups of rpb rows each.
+hipError_t launch_row_slices(QuantFn fn, int rpb, const void *x, int esize, int64_t rows, int K,
+                             int64_t ldx, int8_t *q, int64_t ldq, float *scale,
+                             hipStream_t stream)
+{
+    const int64_t step = kMaxBlocksPerLaunch * rpb;
+    for (int64_t r0 = 0; r0 < rows; r0 += step) {
+        const int64_t n = std::min(rows - r0, step);
+        hipLaunchKernelGGL(fn, dim3((unsigned)ceil_div(n, rpb)), dim3(256), 0, stream,
+                           static_cast<const char *>(x) + r0 * ldx * esize, n, K, ldx,
+                           q + r0 * ldq, ldq, scale + r0);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
 hipError_t launch_quant_rows(const void *x, int kind, int64_t rows, int64_t K, int64_t ldx,
                              int8_t *q, int64_t ldq, float *scale, hipStream_t stream, bool fp8)
 {
     if (rows == 0)
         return hipSuccess;
     const int vec = kind == kF32 ? 4 : 8;
+    const int esize = kind == kF32 ? 4 : 2;
     const int64_t chunks = ceil_div(K, vec);
     // Fewest waves per row that keep the row in registers, unless the grid
     // would then have too few waves to cover the machine's latency.
@@ -189,17 +215,13 @@ hipError_t launch_quant_rows(const void *x, int kind, int64_t rows, int64_t K, i
         QuantFn fn = fp8 ? (kind == kF32 ? pick<kF32, true>(wpr, ch_idx) : pick<kBF16, true>(wpr, ch_idx))
                    : kind == kF32 ? pick<kF32, false>(wpr, ch_idx)
                    : kind == kF16 ? pick<kF16, false>(wpr, ch_idx) : pick<kBF16, false>(wpr, ch_idx);
-        hipLaunchKernelGGL(fn, dim3((unsigned)ceil_div(rows, rpb)), dim3(256), 0, stream, x, rows,
-                           (int)K, ldx, q, ldq, scale);
-        return hipGetLastError();
+        return launch_row_slices(fn, rpb, x, esize, rows, (int)K, ldx, q, ldq, scale, stream);
     }
     QuantFn fn = fp8 ? (kind == kF32 ? quant_rows_looped_kernel<kF32, true>
                               : quant_rows_looped_kernel<kBF16, true>)
                : kind == kF32 ? quant_rows_looped_kernel<kF32, false>
                : kind == kF16 ? quant_rows_looped_kernel<kF16, false> : quant_rows_looped_kernel<kBF16, false>;
-    hipLaunchKernelGGL(fn, dim3((unsigned)rows), dim3(256), 0, stream, x, rows, (int)K, ldx, q,
-                       ldq, scale);
-    return hipGetLastError();
+    return launch_row_slices(fn, 1, x, esize, rows, (int)K, ldx, q, ldq, scale, stream);
 }
 
 }  // namespace w8a8

@@ -35,6 +35,12 @@ const TileEntry &tile_entry(int tile)
 
 int mm_tile_count() { return kNumTiles + skinny_tile_count(); }
 
+bool mm_launch_fits(int tile, int64_t M, int64_t N)
+{
+    const TileEntry &e = tile_entry(tile);
+    return mm_grid_fits(ceil_div(M, e.bm) * ceil_div(N, e.bn), e.threads);
+}
+
 const char *mm_tile_name(int tile)
 {
     return (tile >= 0 && tile < mm_tile_count()) ? tile_entry(tile).name : "";

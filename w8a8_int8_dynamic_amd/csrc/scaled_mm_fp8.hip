@@ -42,6 +42,12 @@ constexpr int kCapKeyBase = 16;
 
 int fp8_tile_count() { return kNumMainTiles + skinny_tile_count(); }
 
+bool fp8_launch_fits(int tile, int64_t M, int64_t N)
+{
+    const TileEntry &e = fp8_entry(tile);
+    return mm_grid_fits(ceil_div(M, e.bm) * ceil_div(N, e.bn), e.threads);
+}
+
 hipError_t launch_quant_scaled_mm_fp8(MmArgs a, int mode, int tile, hipStream_t stream)
 {
     return launch_quant_scaled_mm_entry(a, mode, fp8_entry(tile), kCapKeyBase + tile, stream);
