@@ -560,3 +560,42 @@ def test_binding_errors_on_device(ops):
     with pytest.raises(W8A8Error) as e:
         ops.scaled_mm(xq, torch.ones(4, device=DEV), packed, torch.ones(16, device=DEV), 16)
     assert e.value.status == 2    # K = 72 is not a multiple of 16
+
+
+def test_binding_argument_checks(ops):
+    """The wrappers refuse what the C ABI cannot check: a packed weight too
+    small for (N, K), and out / xq buffers of the wrong shape, for the int8
+    calls and their e4m3 twins."""
+    bf = torch.bfloat16
+    x = torch.zeros((4, 64), dtype=bf, device=DEV)
+    w = torch.zeros((16, 64), device=DEV)
+    packed, ws = ops.quant_prepack_weight(w)
+    packed8, ws8 = ops.fp8_quant_prepack_weight(w)
+    xq, xs = ops.quant_per_token(x)
+    xq8, xs8 = ops.fp8_quant_per_token(x)
+    small = packed[:-16]
+    bad_out = torch.empty((4, 8), dtype=bf, device=DEV)
+    cases = [
+        lambda: ops.scaled_mm(xq, xs, small, ws, 16),
+        lambda: ops.scaled_mm(xq, xs, packed, ws, 16, out=bad_out),
+        lambda: ops.quant_scaled_mm(x, small, ws, 16),
+        lambda: ops.quant_scaled_mm(x, packed, ws, 16, out=bad_out),
+        lambda: ops.quant_scaled_mm(x, packed, ws, 16, xq=torch.empty((4, 32), dtype=torch.int8,
+                                                                      device=DEV)),
+        lambda: ops.quant_per_token(x, xq=torch.empty((4, 32), dtype=torch.int8, device=DEV)),
+        lambda: ops.fp8_scaled_mm(xq8, xs8, packed8[:-16], ws8, 16),
+        lambda: ops.fp8_scaled_mm(xq8, xs8, packed8, ws8, 16, out=bad_out),
+        lambda: ops.fp8_quant_scaled_mm(x, packed8[:-16], ws8, 16),
+        lambda: ops.fp8_quant_scaled_mm(x, packed8, ws8, 16, out=bad_out),
+        lambda: ops.fp8_quant_scaled_mm(x, packed8, ws8, 16,
+                                        xq=torch.empty((4, 32), dtype=torch.uint8, device=DEV)),
+        lambda: ops.fp8_quant_per_token(x, xq=torch.empty((4, 32), dtype=torch.uint8, device=DEV)),
+    ]
+    for i, case in enumerate(cases):
+        with pytest.raises(ValueError):
+            case()
+            pytest.fail(f"case {i} was accepted")
+    # and the well-formed calls still run, the fp8 one with caller buffers
+    out8, q8, s8 = ops.fp8_quant_scaled_mm(x, packed8, ws8, 16, xq=xq8, xs=xs8)
+    assert q8.data_ptr() == xq8.data_ptr() and s8.data_ptr() == xs8.data_ptr()
+    assert out8.shape == (4, 16)

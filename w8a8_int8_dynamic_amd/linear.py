@@ -47,8 +47,9 @@ class W8A8Linear(torch.nn.Module):
 
     @classmethod
     def from_float(cls, weight: torch.Tensor, bias: Optional[torch.Tensor] = None) -> "W8A8Linear":
-        """bf16 and fp32 weights are quantized as they are; other float types
-        (fp16) are widened to fp32 first, which is exact."""
+        """bf16 and fp32 weights are quantized as they are. Other float types
+        are converted to fp32 first: exact for fp16, rounded for fp64 (the
+        quant rule works on fp32 values)."""
         w = weight if weight.dtype in (torch.bfloat16, torch.float32) else weight.to(torch.float32)
         N, K = w.shape
         packed, ws = ops.quant_prepack_weight(w.contiguous())

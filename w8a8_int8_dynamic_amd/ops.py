@@ -49,6 +49,18 @@ def _vector(t: Optional[torch.Tensor], n: int, name: str, dtype: torch.dtype):
     return t
 
 
+def _same_device(ref: torch.Tensor, *others: Optional[torch.Tensor]) -> None:
+    for t in others:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"all tensors must be on {ref.device}, got one on {t.device}")
+
+
+def _packed(w_packed: torch.Tensor, N: int, K: int) -> None:
+    if not w_packed.is_cuda or w_packed.dtype != torch.uint8 or \
+            w_packed.numel() < prepack_weight_bytes(N, K):
+        raise ValueError("w_packed must be a uint8 device buffer of the packed layout (N, K)")
+
+
 def _round_up(a: int, b: int) -> int:
     return -(-a // b) * b
 
@@ -97,7 +109,10 @@ def quant_per_token(x: torch.Tensor, xq: Optional[torch.Tensor] = None,
     if xs is None:
         xs = torch.empty((M,), dtype=torch.float32, device=x.device)
     _matrix(xq, "xq", torch.int8)
+    if xq.shape != (M, K):
+        raise ValueError(f"xq must have shape {(M, K)}")
     _vector(xs, M, "xs", torch.float32)
+    _same_device(x, xq, xs)
     with torch.cuda.device(x.device):
         call("int8_quant_per_token" + _ACT_ENTRY[x.dtype], x.data_ptr(), M, K, _ld(x),
              xq.data_ptr(), _ld(xq), xs.data_ptr(), _stream(x))
@@ -175,9 +190,7 @@ def scaled_mm(xq: torch.Tensor, xs: Optional[torch.Tensor], w_packed: torch.Tens
         _vector(xs, M, "xs", torch.float32)
         _vector(ws, N, "ws", torch.float32)
         _vector(bias, N, "bias", out_dtype)
-    if not w_packed.is_cuda or w_packed.dtype != torch.uint8 or \
-            w_packed.numel() < prepack_weight_bytes(N, K):
-        raise ValueError("w_packed must be a uint8 device buffer from prepack_weight(N, K)")
+    _packed(w_packed, N, K)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=xq.device)
     _matrix(out, "out", out_dtype)
@@ -187,6 +200,7 @@ def scaled_mm(xq: torch.Tensor, xs: Optional[torch.Tensor], w_packed: torch.Tens
     def ptr(t):
         return None if t is None or mode == W8A8_OUT_I32 else t.data_ptr()
 
+    _same_device(xq, w_packed, out, *((xs, ws, bias) if mode != W8A8_OUT_I32 else ()))
     with torch.cuda.device(xq.device):
         call("int8_scaled_mm_tile", xq.data_ptr(), _ld(xq), ptr(xs), w_packed.data_ptr(), ptr(ws),
              ptr(bias), M, N, K, mode, out.data_ptr(), _ld(out), _stream(xq), tile)
@@ -212,9 +226,7 @@ def quant_scaled_mm(x: torch.Tensor, w_packed: torch.Tensor, ws: Optional[torch.
     if mode != W8A8_OUT_I32:
         _vector(ws, N, "ws", torch.float32)
         _vector(bias, N, "bias", out_dtype)
-    if not w_packed.is_cuda or w_packed.dtype != torch.uint8 or \
-            w_packed.numel() < prepack_weight_bytes(N, K):
-        raise ValueError("w_packed must be a uint8 device buffer from prepack_weight(N, K)")
+    _packed(w_packed, N, K)
     if xq is None:
         xq = _codes(M, K, x.device)
     if xs is None:
@@ -232,6 +244,7 @@ def quant_scaled_mm(x: torch.Tensor, w_packed: torch.Tensor, ws: Optional[torch.
     def ptr(t):
         return None if t is None or mode == W8A8_OUT_I32 else t.data_ptr()
 
+    _same_device(x, w_packed, xq, xs, out, *((ws, bias) if mode != W8A8_OUT_I32 else ()))
     with torch.cuda.device(x.device):
         call("int8_quant_scaled_mm" + _ACT_ENTRY[x.dtype] + "_tile", x.data_ptr(), _ld(x),
              xq.data_ptr(), _ld(xq), xs.data_ptr(), w_packed.data_ptr(), ptr(ws), ptr(bias), M,
@@ -257,7 +270,10 @@ def fp8_quant_per_token(x: torch.Tensor, xq: Optional[torch.Tensor] = None,
     xq = _fp8_codes(M, K, x.device) if xq is None else xq
     xs = torch.empty((M,), dtype=torch.float32, device=x.device) if xs is None else xs
     _matrix(xq, "xq", torch.uint8)
+    if xq.shape != (M, K):
+        raise ValueError(f"xq must have shape {(M, K)}")
     _vector(xs, M, "xs", torch.float32)
+    _same_device(x, xq, xs)
     with torch.cuda.device(x.device):
         call("fp8_quant_per_token", x.data_ptr(), M, K, _ld(x), xq.data_ptr(), _ld(xq),
              xs.data_ptr(), _stream(x))
@@ -308,9 +324,7 @@ def fp8_scaled_mm(xq: torch.Tensor, xs: Optional[torch.Tensor], w_packed: torch.
         _vector(xs, M, "xs", torch.float32)
         _vector(ws, N, "ws", torch.float32)
         _vector(bias, N, "bias", out_dtype)
-    if not w_packed.is_cuda or w_packed.dtype != torch.uint8 or \
-            w_packed.numel() < prepack_weight_bytes(N, K):
-        raise ValueError("w_packed must be a uint8 device buffer of the packed layout (N, K)")
+    _packed(w_packed, N, K)
     out = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
     _matrix(out, "out", out_dtype)
     if out.shape != (M, N):
@@ -319,6 +333,7 @@ def fp8_scaled_mm(xq: torch.Tensor, xs: Optional[torch.Tensor], w_packed: torch.
     def ptr(t):
         return None if t is None or mode == W8A8_OUT_I32 else t.data_ptr()
 
+    _same_device(xq, w_packed, out, *((xs, ws, bias) if mode != W8A8_OUT_I32 else ()))
     with torch.cuda.device(xq.device):
         call("fp8_scaled_mm_tile", xq.data_ptr(), _ld(xq), ptr(xs), w_packed.data_ptr(), ptr(ws),
              ptr(bias), M, N, K, mode, out.data_ptr(), _ld(out), _stream(xq), tile)
@@ -328,7 +343,8 @@ def fp8_scaled_mm(xq: torch.Tensor, xs: Optional[torch.Tensor], w_packed: torch.
 def fp8_quant_scaled_mm(x: torch.Tensor, w_packed: torch.Tensor, ws: Optional[torch.Tensor],
                         N: int, bias: Optional[torch.Tensor] = None,
                         out_dtype: torch.dtype = torch.bfloat16,
-                        out: Optional[torch.Tensor] = None, tile: int = -1
+                        out: Optional[torch.Tensor] = None, tile: int = -1,
+                        xq: Optional[torch.Tensor] = None, xs: Optional[torch.Tensor] = None
                         ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """e4m3 per-token quant of bf16 x and the e4m3 scaled matmul: (out, xq, xs).
     out_dtype bf16 or fp16, or float32 for the raw fp32 accumulators."""
@@ -341,13 +357,22 @@ def fp8_quant_scaled_mm(x: torch.Tensor, w_packed: torch.Tensor, ws: Optional[to
     if mode != W8A8_OUT_I32:
         _vector(ws, N, "ws", torch.float32)
         _vector(bias, N, "bias", out_dtype)
-    xq = _fp8_codes(M, K, x.device)
-    xs = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _packed(w_packed, N, K)
+    xq = _fp8_codes(M, K, x.device) if xq is None else xq
+    xs = torch.empty((M,), dtype=torch.float32, device=x.device) if xs is None else xs
+    _matrix(xq, "xq", torch.uint8)
+    if xq.shape != (M, K):
+        raise ValueError(f"xq must have shape {(M, K)}")
+    _vector(xs, M, "xs", torch.float32)
     out = torch.empty((M, N), dtype=out_dtype, device=x.device) if out is None else out
     _matrix(out, "out", out_dtype)
+    if out.shape != (M, N):
+        raise ValueError(f"out must have shape {(M, N)}")
+
     def ptr(t):
         return None if t is None or mode == W8A8_OUT_I32 else t.data_ptr()
 
+    _same_device(x, w_packed, xq, xs, out, *((ws, bias) if mode != W8A8_OUT_I32 else ()))
     with torch.cuda.device(x.device):
         call("fp8_quant_scaled_mm_tile", x.data_ptr(), _ld(x), xq.data_ptr(), _ld(xq),
              xs.data_ptr(), w_packed.data_ptr(), ptr(ws), ptr(bias), M, N, K, mode,
