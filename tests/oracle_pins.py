@@ -605,8 +605,82 @@ def pin_pages_missing_act_scale(o, rows: int = 64):
     assert abs(fro / float(xs.mean()) - 1) < 1e-3
 
 
+def _round_binary(v: Fraction, sig: int, emin: int) -> Fraction:
+    """v rounded to nearest-even in a binary format with `sig` significant
+    bits and gradual underflow below 2^emin (the IEEE rule, on exact
+    rationals; no overflow handling: the callers stay in range)."""
+    if v == 0:
+        return v
+    neg = v < 0
+    a = -v if neg else v
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    ulp = Fraction(2) ** (max(e, emin) - (sig - 1))
+    t = a / ulp
+    r = int(t)
+    frac = t - r
+    if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and r % 2 == 1):
+        r += 1
+    return -(r * ulp) if neg else r * ulp
+
+
+def _fl32(v: Fraction) -> Fraction:
+    return _round_binary(v, 24, -126)
+
+
+def _order_sensitive_inputs(n: int, seed: int, out_bits: int, limit: float):
+    """Seeded (acc, xs, ws) triples whose result, rounded to `out_bits`
+    significant bits, depends on the order of the two scale products:
+    (acc*xs)*ws, (acc*ws)*xs and acc*(xs*ws) in fp32 do not all round to the
+    same output. NumPy's float32 arithmetic (IEEE, round to nearest) finds
+    them; the pin then checks the oracle against the exact model. Results of
+    magnitude `limit` or more are left out (fp16 overflows at 65520)."""
+    rng = np.random.default_rng(seed)
+    acc = rng.integers(-2 ** 26, 2 ** 26, n).astype(np.int64)
+    xs = rng.uniform(1e-3, 1.0, n).astype(np.float32)
+    ws = rng.uniform(1e-5, 1e-2, n).astype(np.float32)
+    a = acc.astype(np.float32)
+    r1 = (a * xs) * ws
+    r2 = (a * ws) * xs
+    r3 = a * (xs * ws)
+
+    def out(r):   # round the fp32 values to out_bits significant bits, nearest-even
+        m, e = np.frexp(r.astype(np.float64))
+        return np.ldexp(np.round(np.ldexp(m, out_bits)), e - out_bits)
+    o1 = out(r1)
+    pick = np.nonzero(((o1 != out(r2)) | (o1 != out(r3))) & (np.abs(r1) < limit))[0]
+    return acc[pick], xs[pick], ws[pick]
+
+
+def pin_epilogue_order(o):
+    """The fp32 epilogue takes its steps in the stated order, each rounded
+    once to fp32: fl(fl(fl(acc)*xs)*ws) (+bias), then one rounding to bf16 or
+    fp16. Checked on inputs where another order gives another output, against
+    an exact rational model of IEEE fp32 rounding; the fp8 epilogue (the same
+    steps on fl32 of its exact sums) too."""
+    for out_bits, fn, exact, limit in ((8, "epilogue_f32", _exact_bf16, np.inf),
+                                       (11, "epilogue_f32_f16", _exact_f16, 6.0e4)):
+        acc, xs, ws = _order_sensitive_inputs(1 << 22, 1500 + out_bits, out_bits, limit)
+        assert len(acc) >= 8, len(acc)          # the inputs do tell the orders apart
+        acc, xs, ws = acc[:64], xs[:64], ws[:64]
+        k = len(acc)
+        # a k x k accumulator matrix whose diagonal holds the cases: output
+        # (i, i) takes acc[i], xs[i] and ws[i]
+        got = getattr(o, fn)(np.diag(acc).astype(np.int32), xs, ws)
+        for i in range(k):
+            t = _fl32(Fraction(int(acc[i])))
+            t = _fl32(t * Fraction(float(xs[i])))
+            t = _fl32(t * Fraction(float(ws[i])))
+            assert got[i, i] == exact(t), (fn, i)
+        if out_bits == 8:
+            own, _ = o.fp8_epilogue(np.diag(acc).astype(np.float64), xs, ws)
+            assert np.array_equal(np.diag(own), np.diag(got)), "fp8 epilogue order"
+
+
 FAST_PINS = [pin_quant_ties, pin_quant_zero_rows, pin_quant_invariants, pin_gemm_bruteforce,
-             pin_gemm_numpy, pin_bf16_rounding, pin_epilogue_exact, pin_f16_conversions,
+             pin_gemm_numpy, pin_bf16_rounding, pin_epilogue_exact, pin_epilogue_order,
+             pin_f16_conversions,
              pin_quant_f16, pin_epilogue_f16_exact, pin_e4m3_conversions, pin_fp8_quant,
              pin_fp8_gemm, pin_fp8_epilogue, pin_layer_vs_numpy, pin_fused_qkv_stack]
 PAGE_PINS = [pin_pages_rel_l2, pin_pages_missing_act_scale]

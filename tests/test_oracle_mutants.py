@@ -51,6 +51,17 @@ MUTANTS = {
                             "s += e4m3_to_double(ar[k]) * (double)br[k];"),
     "fp8_epilogue_drops_xs": ("double d = acc[m * ldc + n] * (double)xs[m] * (double)ws[n];",
                               "double d = acc[m * ldc + n] * (double)ws[n];"),
+    "epilogue_scales_swapped": ("t = t * xs[m];\n            t = t * ws[n];",
+                                "t = t * ws[n];\n            t = t * xs[m];"),
+    "epilogue_scales_fused": ("t = t * xs[m];\n            t = t * ws[n];",
+                              "t = t * (xs[m] * ws[n]);"),
+    "fp8_sign_dropped": ("uint8_t sign = signbit(d) ? 0x80u : 0x00u;", "uint8_t sign = 0x00u;"),
+    "fp8_zero_loses_sign": ("if (a == 0.0)\n        return sign;", "if (a == 0.0)\n        return 0;"),
+    "fp8_underflow_loses_sign": ("if (r == 0.0)\n        return sign;", "if (r == 0.0)\n        return 0;"),
+    "fp8_exponent_bias_8": ("((exp_unbiased + 7) << 3)", "((exp_unbiased + 8) << 3)"),
+    "fp8_subnormal_boundary": ("if (exp_unbiased < -6)", "if (exp_unbiased < -7)"),
+    "fp8_no_zero_row_rule": ("if (a < 0x1p-100f) {\n        *scale = 0.0f;\n        for (int64_t k = 0; k < K; ++k)\n            q[k] = 0;\n        return;\n    }\n    float s = a / 448.0f;",
+                             "if (a < 0.0f) {\n        *scale = 0.0f;\n        for (int64_t k = 0; k < K; ++k)\n            q[k] = 0;\n        return;\n    }\n    float s = a / 448.0f;"),
 }
 
 
