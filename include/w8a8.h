@@ -8,8 +8,11 @@
  * int32 matmul, and a scale epilogue back to bf16. The same page's kernel-path
  * paragraph names the two run-time ops (a per-token quant, then a scaled
  * matmul) and the load-time transpose-repack of the weight; this header
- * exposes exactly those three steps, plus the offline weight quantization
- * that produces the int8 weights and a debug unpack of the repacked weight.
+ * exposes those three steps, the offline weight quantization that produces
+ * the int8 weights and a debug unpack of the repacked weight. Beyond them:
+ * the quant and the matmul in one call (int8_quant_scaled_mm), fp16
+ * activations and outputs, the online weight quant straight into the
+ * repacked layout, and an FP8 (e4m3) twin of the whole path.
  *
  * Conventions for every entry point:
  *   - Pointers to tensors are DEVICE pointers on the current HIP device.
@@ -25,8 +28,12 @@
  *   - All argument checks run on the host before any HIP call, so a bad
  *     argument returns an error without touching the device. There is no
  *     fallback path: an unsupported device or argument is an error.
- *   - Calls are thread-safe; the only shared state is a per-device cache of
- *     the "is this a gfx950" answer and a thread-local error message.
+ *   - Calls are thread-safe. Shared host state is atomic: per-device caches
+ *     (the "is this a gfx950" answer, the fused kernels' resident-workgroup
+ *     capacity) and a per-device launch counter for the fused kernels'
+ *     flags; the error message is thread-local. The only library-owned
+ *     device memory is those flags, a static array (see
+ *     int8_quant_scaled_mm).
  */
 #ifndef W8A8_H
 #define W8A8_H
