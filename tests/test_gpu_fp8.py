@@ -294,3 +294,33 @@ def test_fp8_full_size_fused_qkv(ops, orc):
     _, ref64 = orc.fp8_epilogue(exact, xs_ref[rows], ws_ref, inp.bias_bf16)
     check_out(bits_np(out)[rows], ref64, "fused_qkv fp8",
               xs_ref[rows].astype(np.float64)[:, None] * ws_ref[None, :] * bound)
+
+
+def test_fp8_linear_layer(ops, orc):
+    """W8A8Linear with scheme "fp8": the weight quantized online to e4m3, the
+    forward equal to fp8_quant_scaled_mm bit for bit and within tolerance of
+    the oracle's exact pipeline; leading dimensions kept; fp16 activations
+    refused."""
+    from w8a8_int8_dynamic_amd import W8A8Linear
+    M, N, K = 96, 200, 640
+    inp = wl.random_case(M, K, N, 8700, bias=True)
+    layer = W8A8Linear.from_float(torch.from_numpy(inp.w_f32).to(DEV), bf16_dev(inp.bias_bf16),
+                                  scheme="fp8")
+    x = bf16_dev(inp.x_bf16)
+    y = layer(x.view(2, M // 2, K))
+    assert y.shape == (2, M // 2, N) and y.dtype == torch.bfloat16
+    ref, _, _ = ops.fp8_quant_scaled_mm(x, layer.w_packed, layer.w_scale, N, layer.bias)
+    assert torch.equal(y.reshape(M, N).view(torch.int16), ref.view(torch.int16))
+    wq, ws_ref = orc.fp8_quant_per_channel(inp.w_f32)
+    assert np.array_equal(layer.w_scale.cpu().numpy(), ws_ref)
+    xq, xs = orc.fp8_quant_per_token(inp.x_bf16)
+    exact = orc.fp8_gemm(xq, wq)
+    _, ref64 = orc.fp8_epilogue(exact, xs, ws_ref, inp.bias_bf16)
+    acc = ops.fp8_scaled_mm(torch.from_numpy(xq).to(DEV), None, layer.w_packed, None, N,
+                            out_dtype=torch.float32).cpu().numpy()
+    bound = check_acc(orc, acc, xq, wq, exact, "fp8 layer")
+    check_out(bits_np(y.reshape(M, N)), ref64, "fp8 layer",
+              xs.astype(np.float64)[:, None] * ws_ref[None, :] * bound)
+    with pytest.raises(TypeError):
+        layer(x.to(torch.float16))
+    assert "scheme=fp8" in repr(layer)

@@ -18,7 +18,11 @@ __all__ = ["W8A8Linear"]
 
 
 class W8A8Linear(torch.nn.Module):
-    """y = int8(x) @ int8(W)^T * x_scale * w_scale (+ bias), in x's type (bf16 or fp16).
+    """y = q(x) @ q(W)^T * x_scale * w_scale (+ bias), in x's type.
+
+    scheme "int8" (the default): int8 codes, bf16 or fp16 activations.
+    scheme "fp8": the e4m3 twin (page "Online Quantization": FP8 W8A8 with
+    dynamic per-token activation scales), bf16 activations.
 
     Build with ``from_float`` (online per-channel weight quantization on the
     GPU, written straight into the load-time layout) or ``from_quantized``
@@ -26,8 +30,11 @@ class W8A8Linear(torch.nn.Module):
     """
 
     def __init__(self, w_packed: torch.Tensor, w_scale: torch.Tensor, out_features: int,
-                 in_features: int, bias: Optional[torch.Tensor] = None):
+                 in_features: int, bias: Optional[torch.Tensor] = None, scheme: str = "int8"):
         super().__init__()
+        if scheme not in ("int8", "fp8"):
+            raise ValueError(f"scheme must be 'int8' or 'fp8', got {scheme!r}")
+        self.scheme = scheme
         self.in_features = in_features
         self.out_features = out_features
         self.register_buffer("w_packed", w_packed)
@@ -46,16 +53,18 @@ class W8A8Linear(torch.nn.Module):
         return cls(packed, w_scale.to(torch.float32).contiguous(), N, K, bias)
 
     @classmethod
-    def from_float(cls, weight: torch.Tensor, bias: Optional[torch.Tensor] = None) -> "W8A8Linear":
+    def from_float(cls, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                   scheme: str = "int8") -> "W8A8Linear":
         """bf16 and fp32 weights are quantized as they are. Other float types
         are converted to fp32 first: exact for fp16, rounded for fp64 (the
         quant rule works on fp32 values)."""
         w = weight if weight.dtype in (torch.bfloat16, torch.float32) else weight.to(torch.float32)
         N, K = w.shape
-        packed, ws = ops.quant_prepack_weight(w.contiguous())
+        quant = ops.fp8_quant_prepack_weight if scheme == "fp8" else ops.quant_prepack_weight
+        packed, ws = quant(w.contiguous())
         if not torch.isfinite(ws).all():
             raise ValueError("weight scales must be finite")
-        return cls(packed, ws, N, K, bias)
+        return cls(packed, ws, N, K, bias, scheme)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         if x.shape[-1] != self.in_features:
@@ -67,9 +76,16 @@ class W8A8Linear(torch.nn.Module):
         # The per-token quant and the scaled matmul, as one library call; the
         # output (and bias) type is x's.
         bias = self.bias_f16 if x2.dtype == torch.float16 else self.bias
-        out, _, _ = ops.quant_scaled_mm(x2, self.w_packed, self.w_scale, self.out_features, bias)
+        if self.scheme == "fp8":
+            if x2.dtype != torch.bfloat16:
+                raise TypeError(f"the fp8 scheme takes bfloat16 activations, got {x2.dtype}")
+            out, _, _ = ops.fp8_quant_scaled_mm(x2, self.w_packed, self.w_scale,
+                                                self.out_features, bias)
+        else:
+            out, _, _ = ops.quant_scaled_mm(x2, self.w_packed, self.w_scale, self.out_features,
+                                            bias)
         return out.reshape(*lead, self.out_features)
 
     def extra_repr(self) -> str:
         return (f"in_features={self.in_features}, out_features={self.out_features}, "
-                f"bias={self.bias is not None}")
+                f"bias={self.bias is not None}, scheme={self.scheme}")
