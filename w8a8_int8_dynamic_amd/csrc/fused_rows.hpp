@@ -13,7 +13,9 @@
 // a shared word, which would serialize at the memory side. The wait is
 // bounded; past the bound a workgroup quantizes the rows it needs itself,
 // writing the same bytes their producers write, so no wave can spin forever
-// and launches that overlap on one device stay correct.
+// and launches that overlap on one device stay correct. The epoch is fixed
+// when the launch is made, so a captured graph would replay it; the host
+// therefore never uses this path on a stream under capture.
 //
 // Coherence. Codes and scales are written with agent-scope (relaxed atomic)
 // stores, coherent across the XCDs once complete, so no write-back of the
