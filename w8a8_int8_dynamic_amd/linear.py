@@ -8,13 +8,14 @@ dimension is contiguous) and outputs come back as [..., N].
 """
 from __future__ import annotations
 
-from typing import Optional
+import fnmatch
+from typing import Optional, Sequence
 
 import torch
 
 from . import ops
 
-__all__ = ["W8A8Linear"]
+__all__ = ["W8A8Linear", "quantize_linear_layers"]
 
 
 class W8A8Linear(torch.nn.Module):
@@ -89,3 +90,45 @@ class W8A8Linear(torch.nn.Module):
     def extra_repr(self) -> str:
         return (f"in_features={self.in_features}, out_features={self.out_features}, "
                 f"bias={self.bias is not None}, scheme={self.scheme}")
+
+
+def quantize_linear_layers(module: torch.nn.Module, method: str = "int8",
+                           activation_scheme: str = "dynamic",
+                           ignored_layers: Sequence[str] = ()) -> torch.nn.Module:
+    """Replace the torch.nn.Linear layers of `module` by W8A8Linear layers.
+
+    The selection follows the page "Online Quantization" (Parameters table):
+    `method` is "int8" or "fp8"; `activation_scheme` must be "dynamic"
+    (activation scales computed per token at run time, the only scheme
+    implemented); `ignored_layers` holds name patterns of layers to keep in
+    their float type. A layer is kept when its qualified name (as in
+    module.named_modules()) matches a pattern by fnmatch or contains it.
+    Weights are quantized online on their device (W8A8Linear.from_float).
+    Anything the path cannot run raises ValueError naming the layer: a layer
+    on the CPU, or in_features not a multiple of 16. Returns `module`, or the
+    replacement when `module` is itself a Linear."""
+    if method not in ("int8", "fp8"):
+        raise ValueError(f"method must be 'int8' or 'fp8', got {method!r}")
+    if activation_scheme != "dynamic":
+        raise ValueError(f"only activation_scheme='dynamic' is implemented, got {activation_scheme!r}")
+    patterns = [p for p in ignored_layers if p]
+
+    def kept(name: str) -> bool:
+        return any(fnmatch.fnmatchcase(name, p) or p in name for p in patterns)
+
+    def convert(name: str, lin: torch.nn.Linear) -> W8A8Linear:
+        if not lin.weight.is_cuda:
+            raise ValueError(f"layer {name!r} is on {lin.weight.device}; move the model to the GPU first")
+        if lin.in_features % 16 != 0:
+            raise ValueError(f"layer {name!r}: in_features {lin.in_features} is not a multiple of 16")
+        bias = None if lin.bias is None else lin.bias.detach()
+        return W8A8Linear.from_float(lin.weight.detach(), bias, scheme=method)
+
+    if isinstance(module, torch.nn.Linear):
+        return module if kept("") else convert("", module)
+    for parent_name, parent in list(module.named_modules()):
+        for child_name, child in list(parent.named_children()):
+            name = f"{parent_name}.{child_name}" if parent_name else child_name
+            if isinstance(child, torch.nn.Linear) and not kept(name):
+                setattr(parent, child_name, convert(name, child))
+    return module
