@@ -377,8 +377,8 @@ def test_workload_full_size(ops, orc, name):
 
 
 # ---------------------------------------------------------------------------
-# Per-token quant and scaled matmul in one call (cooperative single launch
-# where the grid fits the device, two launches otherwise)
+# Per-token quant and scaled matmul in one call (one launch where the grid
+# fits the device, two launches otherwise)
 # ---------------------------------------------------------------------------
 QMM_SHAPES = [(1, 48, 64), (37, 45, 80), (130, 200, 336), (257, 300, 1040), (512, 520, 576),
               (512, 1536, 512), (2, 1000, 4112), (1, 300, 16384)]
