@@ -348,6 +348,15 @@ int w8a8_mm_tile_count(void);
 const char *w8a8_mm_tile_name(int tile);
 int w8a8_mm_tile_auto(int64_t M, int64_t N, int64_t K);
 
+/* Bound on the polls (about 1 us each; default 4096) that a workgroup of the
+ * one-launch path of int8_quant_scaled_mm / fp8_quant_scaled_mm makes for
+ * the producers of its tile's rows before it quantizes those rows itself.
+ * For tests and diagnosis: 0 sends every workgroup down that path at once,
+ * with results unchanged. polls >= 0 sets the bound for launches made after
+ * the call (process wide, every device) and returns the previous bound; a
+ * negative value only returns the current one. */
+int w8a8_fused_wait_limit(int polls);
+
 /* 1 when `device` is a gfx950 GPU this library can run on, else 0. */
 int w8a8_device_supported(int device);
 

@@ -262,6 +262,20 @@ def test_no_fallback_without_device():
     assert "device" in _lib.last_error()
 
 
+def test_fused_wait_limit_setter():
+    """The bound on the fused path's polls: query, set, restore (host only)."""
+    cur = L.w8a8_fused_wait_limit(-1)
+    assert cur == 4096
+    try:
+        assert L.w8a8_fused_wait_limit(0) == cur
+        assert L.w8a8_fused_wait_limit(-1) == 0
+        assert L.w8a8_fused_wait_limit(7) == 0
+        assert L.w8a8_fused_wait_limit(-5) == 7
+    finally:
+        L.w8a8_fused_wait_limit(cur)
+    assert L.w8a8_fused_wait_limit(-1) == cur
+
+
 def test_tile_table():
     n = L.w8a8_mm_tile_count()
     assert n >= 4

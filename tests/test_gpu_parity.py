@@ -599,3 +599,42 @@ def test_binding_argument_checks(ops):
     out8, q8, s8 = ops.fp8_quant_scaled_mm(x, packed8, ws8, 16, xq=xq8, xs=xs8)
     assert q8.data_ptr() == xq8.data_ptr() and s8.data_ptr() == xs8.data_ptr()
     assert out8.shape == (4, 16)
+
+
+def test_quant_scaled_mm_own_rows_path(ops, orc):
+    """The one-launch path's bounded wait run out at once (bound 0, set from
+    the host): every workgroup quantizes its tile's rows itself instead of
+    waiting for their producers. Codes, scales and outputs stay bit-exact to
+    the oracle on every main tile, int8 and e4m3."""
+    from w8a8_int8_dynamic_amd import _lib
+    L = _lib.lib()
+    main = [t for t in range(ops.tile_count()) if not ops.tile_name(t).startswith("s")]
+    cases = []
+    for i, (M, N, K) in enumerate([(512, 1536, 512), (257, 300, 1040), (130, 200, 336)]):
+        inp = wl.random_case(M, K, N, 9500 + i, bias=True)
+        wq_ref, ws_ref = orc.quant_per_channel(inp.w_f32)
+        xq_ref, xs_ref = orc.quant_per_token(inp.x_bf16)
+        ref32 = orc.epilogue_f32(orc.gemm_i32(xq_ref, wq_ref), xs_ref, ws_ref, inp.bias_bf16)
+        packed = ops.prepack_weight(torch.from_numpy(wq_ref).to(DEV))
+        cases.append((inp, N, packed, torch.from_numpy(ws_ref).to(DEV), xq_ref, xs_ref, ref32))
+    inp8 = cases[0][0]
+    packed8, ws8 = ops.fp8_quant_prepack_weight(torch.from_numpy(inp8.w_f32).to(DEV))
+    x8, b8 = bf16_dev(inp8.x_bf16), bf16_dev(inp8.bias_bf16)
+    waited = [ops.fp8_quant_scaled_mm(x8, packed8, ws8, cases[0][1], b8, tile=t)[0].clone()
+              for t in main]
+    prev = L.w8a8_fused_wait_limit(0)
+    try:
+        for inp, N, packed, ws, xq_ref, xs_ref, ref32 in cases:
+            x, b = bf16_dev(inp.x_bf16), bf16_dev(inp.bias_bf16)
+            for t in main:
+                out, xq, xs = ops.quant_scaled_mm(x, packed, ws, N, b, tile=t)
+                torch.cuda.synchronize()
+                name = f"{ops.tile_name(t)} {inp.x_bf16.shape}"
+                assert np.array_equal(xq.cpu().numpy(), xq_ref), name
+                assert np.array_equal(xs.cpu().numpy(), xs_ref), name
+                assert np.array_equal(bits_np(out), ref32), name
+        for t, ref in zip(main, waited):
+            out8, _, _ = ops.fp8_quant_scaled_mm(x8, packed8, ws8, cases[0][1], b8, tile=t)
+            assert torch.equal(out8.view(torch.int16), ref.view(torch.int16)), ops.tile_name(t)
+    finally:
+        L.w8a8_fused_wait_limit(prev)

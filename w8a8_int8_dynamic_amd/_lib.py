@@ -57,6 +57,7 @@ SIGNATURES = {
     "fp8_quant_scaled_mm_tile": (_int, [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64,
                                         _i64, _int, _vp, _i64, _vp, _int]),
     "w8a8_fp8_tile_count": (_int, []),
+    "w8a8_fused_wait_limit": (_int, [_int]),
     "w8a8_fp8_tile_auto": (_int, [_i64, _i64, _i64]),
     "w8a8_mm_tile_count": (_int, []),
     "w8a8_mm_tile_name": (ctypes.c_char_p, [_int]),

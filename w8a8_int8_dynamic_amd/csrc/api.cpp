@@ -536,6 +536,12 @@ W8A8_API int w8a8_mm_tile_auto(int64_t M, int64_t N, int64_t K)
     return w8a8::mm_tile_auto(M, N, K);
 }
 
+W8A8_API int w8a8_fused_wait_limit(int polls)
+{
+    return polls >= 0 ? (int)w8a8::set_fused_wait_limit((unsigned)polls)
+                      : (int)w8a8::fused_wait_limit();
+}
+
 W8A8_API int w8a8_device_supported(int device) { return query_supported(device); }
 
 W8A8_API const char *w8a8_status_string(int status)

@@ -39,9 +39,11 @@ using quant_rule::u32;
 constexpr int kMaxProducers = 16384;
 static __device__ unsigned g_flag[kMaxProducers];
 
-// Bound on the polls for a tile's rows (each ~1 us; a few ms in all): far
-// beyond any real wait.
-constexpr int kSpinLimit = 1 << 12;
+// Default bound on the polls for a tile's rows (each ~1 us; a few ms in
+// all): far beyond any real wait. A launch carries its bound in
+// MmArgs::wait_limit, which the host can lower (0 makes every workgroup take
+// its own-rows path at once, which tests use).
+constexpr unsigned kDefaultWaitLimit = 1u << 12;
 
 // Short rows (K <= 64 * 8 * CPL): one wavefront per row, CPL 16-byte chunks
 // per lane, 8 / CPL rows per wavefront in flight (all their loads issued
@@ -242,8 +244,9 @@ __device__ __forceinline__ bool wait_producers(const MmArgs &a, int p0, int coun
 {
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
-        int it = 0;
-        for (; it < kSpinLimit; ++it) {
+        const unsigned limit = a.wait_limit;
+        unsigned it = 0;
+        for (; it < limit; ++it) {
             bool ready = true;
             for (int i = lane; i < count; i += 64)
                 ready &= __hip_atomic_load(&g_flag[p0 + i], __ATOMIC_RELAXED,
@@ -253,7 +256,7 @@ __device__ __forceinline__ bool wait_producers(const MmArgs &a, int p0, int coun
             __builtin_amdgcn_s_sleep(2);
         }
         if (lane == 0)
-            decision[0] = it == kSpinLimit;
+            decision[0] = it == limit;
     }
     __syncthreads();
     return decision[0] != 0;

@@ -67,7 +67,8 @@ struct MmArgs {
     const uint16_t *x;
     int64_t ldx;
     int rows_per_wg;
-    unsigned epoch;  // this launch's number on its device, never 0
+    unsigned epoch;       // this launch's number on its device, never 0
+    unsigned wait_limit;  // bound on a workgroup's polls for its producers' flags
 };
 
 // Output kinds, the ABI's W8A8_OUT_* values: they index TileEntry's kernels.
@@ -125,6 +126,10 @@ hipError_t launch_scaled_mm(const MmArgs &a, int mode, int tile, hipStream_t str
 // launched) when the shape's workgroups cannot all be resident at once; the
 // caller then runs the two steps as separate launches.
 hipError_t launch_quant_scaled_mm(MmArgs a, int mode, int tile, hipStream_t stream);
+// The bound on the polls of the fused launches made from now on (process
+// wide); returns the previous bound.
+unsigned set_fused_wait_limit(unsigned polls);
+unsigned fused_wait_limit();
 // The same for any tile entry; cap_key (< 32) names it in the per-device
 // cache of resident-workgroup capacities.
 hipError_t launch_quant_scaled_mm_entry(MmArgs a, int mode, const TileEntry &e, int cap_key,

@@ -230,6 +230,7 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
         a.ldx = pinned(args.ldx);
         a.rows_per_wg = pinned(args.rows_per_wg);
         a.epoch = pinned(args.epoch);
+        a.wait_limit = pinned(args.wait_limit);
     }
 
     const int lane = threadIdx.x & 63;

@@ -126,6 +126,14 @@ static hipError_t fused_capacity(int dev, int tile, int mode, MmKernel fn, int t
     return hipSuccess;
 }
 
+namespace {
+std::atomic<unsigned> g_wait_limit{fused::kDefaultWaitLimit};
+}  // namespace
+
+unsigned set_fused_wait_limit(unsigned polls) { return g_wait_limit.exchange(polls); }
+
+unsigned fused_wait_limit() { return g_wait_limit.load(); }
+
 hipError_t launch_quant_scaled_mm(MmArgs a, int mode, int tile, hipStream_t stream)
 {
     return launch_quant_scaled_mm_entry(a, mode, tile_entry(tile), tile, stream);
@@ -181,6 +189,7 @@ hipError_t launch_quant_scaled_mm_entry(MmArgs a, int mode, const TileEntry &e, 
     if (v == 0)
         v = ++ep;
     a.epoch = v;
+    a.wait_limit = g_wait_limit.load();
     hipLaunchKernelGGL(fn, dim3((unsigned)tiles), dim3(e.threads), 0, stream, a);
     return hipGetLastError();
 }
