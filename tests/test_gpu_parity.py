@@ -638,3 +638,34 @@ def test_quant_scaled_mm_own_rows_path(ops, orc):
             assert torch.equal(out8.view(torch.int16), ref.view(torch.int16)), ops.tile_name(t)
     finally:
         L.w8a8_fused_wait_limit(prev)
+
+
+def test_quant_scaled_mm_overlapping_streams(ops, orc):
+    """Single-launch calls on two streams at once share the producer-flag
+    words; each launch accepts only its own launch number, so a clobbered
+    wait runs out and the workgroup quantizes its rows itself. Every call's
+    codes, scales and outputs must match the oracle for its own input."""
+    M, N, K = 512, 1536, 1024
+    cases = []
+    for i in range(2):
+        inp = wl.random_case(M, K, N, 9600 + i, bias=True)
+        wq_ref, ws_ref = orc.quant_per_channel(inp.w_f32)
+        xq_ref, xs_ref = orc.quant_per_token(inp.x_bf16)
+        ref32 = orc.epilogue_f32(orc.gemm_i32(xq_ref, wq_ref), xs_ref, ws_ref, inp.bias_bf16)
+        packed = ops.prepack_weight(torch.from_numpy(wq_ref).to(DEV))
+        cases.append((bf16_dev(inp.x_bf16), packed, torch.from_numpy(ws_ref).to(DEV),
+                      bf16_dev(inp.bias_bf16), xq_ref, xs_ref, ref32))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    results = []
+    for it in range(8):
+        for k, s in enumerate(streams):
+            x, packed, ws, b, *_ = cases[k]
+            with torch.cuda.stream(s):
+                results.append((k, ops.quant_scaled_mm(x, packed, ws, N, b)))
+    torch.cuda.synchronize()
+    for k, (out, xq, xs) in results:
+        _, _, _, _, xq_ref, xs_ref, ref32 = cases[k]
+        assert np.array_equal(xq.cpu().numpy(), xq_ref) and np.array_equal(xs.cpu().numpy(), xs_ref)
+        assert np.array_equal(bits_np(out), ref32)
