@@ -217,3 +217,29 @@ def test_fused_qkv_full_size_f16(ops, orc):
     ref64 = orc.epilogue_f64_f16(acc, xs_ref[rows], ws_ref, b16)
     exact = check_out16(bits_np(out)[rows], ref32, ref64, "fused_qkv f16")
     assert exact == 1.0
+
+
+def test_f16_output_range_edges(ops, orc):
+    """fp16 outputs across the whole range on every tile: row scales from
+    1e-14 to 1e4 put outputs in fp16's subnormal range, around its largest
+    finite value and past it (infinity from 65520). Bit-exact to the
+    oracle's fp16 epilogue, infinities and signed zeros included."""
+    M, N, K = 80, 136, 320
+    rng = np.random.default_rng(8800)
+    xq = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    wq = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    xs = (10.0 ** np.linspace(-14, 4, M)).astype(np.float32)
+    ws = (rng.uniform(0.5, 2.0, N) * 1e-2).astype(np.float32)
+    bias = np.where(np.arange(N) % 3 == 0, 0.0, rng.standard_normal(N) * 1e-6).astype(np.float16)
+    b16 = bias.view(np.uint16)
+    acc = orc.gemm_i32(xq, wq)
+    ref = orc.epilogue_f32_f16(acc, xs, ws, b16)
+    assert np.isinf(ref.view(np.float16)).any()              # the cases are there
+    assert ((ref & 0x7C00) == 0).any() and ((ref & 0x03FF) != 0).any()
+    xq_d = torch.from_numpy(xq).to(DEV)
+    packed = ops.prepack_weight(torch.from_numpy(wq).to(DEV))
+    xs_d, ws_d = torch.from_numpy(xs).to(DEV), torch.from_numpy(ws).to(DEV)
+    b_d = torch.from_numpy(bias).to(DEV)
+    for t in range(ops.tile_count()):
+        out = ops.scaled_mm(xq_d, xs_d, packed, ws_d, N, b_d, out_dtype=torch.float16, tile=t)
+        assert np.array_equal(bits_np(out), ref), ops.tile_name(t)

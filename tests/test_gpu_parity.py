@@ -669,3 +669,27 @@ def test_quant_scaled_mm_overlapping_streams(ops, orc):
         _, _, _, _, xq_ref, xs_ref, ref32 = cases[k]
         assert np.array_equal(xq.cpu().numpy(), xq_ref) and np.array_equal(xs.cpu().numpy(), xs_ref)
         assert np.array_equal(bits_np(out), ref32)
+
+
+def test_bf16_output_range_edges(ops, orc):
+    """bf16 outputs across fp32's range on every tile: caller scales from
+    1e-40 to 1e30 (and channel scales of 1e-30) take the fixed-order fp32
+    epilogue into subnormals, to signed zeros and up to about 1e33. Bit-exact to the oracle's fp32 epilogue, signed zeros and
+    subnormal results included."""
+    M, N, K = 80, 136, 320
+    rng = np.random.default_rng(8900)
+    xq = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    wq = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    xs = (10.0 ** np.linspace(-40, 30, M)).astype(np.float32)
+    ws = (rng.uniform(0.5, 2.0, N) * 1e-2).astype(np.float32)
+    ws[::17] = np.float32(1e-30)                  # products that underflow to signed zeros
+    acc = orc.gemm_i32(xq, wq)
+    ref = orc.epilogue_f32(acc, xs, ws)
+    assert ((ref & 0x7F80) == 0).any() and ((ref & 0x007F) != 0).any()   # bf16 subnormals
+    assert (ref == 0x8000).any()                                         # negative zeros
+    xq_d = torch.from_numpy(xq).to(DEV)
+    packed = ops.prepack_weight(torch.from_numpy(wq).to(DEV))
+    xs_d, ws_d = torch.from_numpy(xs).to(DEV), torch.from_numpy(ws).to(DEV)
+    for t in range(ops.tile_count()):
+        out = ops.scaled_mm(xq_d, xs_d, packed, ws_d, N, tile=t)
+        assert np.array_equal(bits_np(out), ref), ops.tile_name(t)
