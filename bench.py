@@ -112,6 +112,75 @@ def settle(torch, fn, seconds: float = 0.3) -> None:
         torch.cuda.synchronize()
 
 
+def time_each(torch, fn, iters: int):
+    """Median and minimum microseconds of single launches of fn, each
+    bracketed by its own pair of HIP events on the launch stream. An isolated
+    launch pays its own ramp and the events' cost, so these sit above the
+    back-to-back mean that the throughput figures use."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    return round(float(np.median(us)), 3), round(us[0], 3)
+
+
+def sclk_under_load(torch, fn, seconds: float = 1.0) -> dict:
+    """The shader clock while fn runs back to back: amd-smi's per-XCD gfx
+    clocks, sampled a few times from the host while another thread keeps
+    the GPU busy. None fields when amd-smi is unavailable."""
+    import subprocess
+    import threading
+    stop = threading.Event()
+
+    def busy():
+        while not stop.is_set():
+            for _ in range(64):
+                fn()
+            torch.cuda.synchronize()
+
+    t = threading.Thread(target=busy)
+    t.start()
+    samples, err = [], None
+    try:
+        time.sleep(0.2)
+        end = time.perf_counter() + seconds
+        while time.perf_counter() < end:
+            r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
+                               text=True, timeout=10)
+            if r.returncode != 0:
+                err = r.stderr.strip()[:120]
+                break
+            data = json.loads(r.stdout)
+            gpus = data["gpu_data"] if isinstance(data, dict) else data
+            clk = gpus[0]["clock"]
+            samples.append([v["clk"]["value"] for k, v in sorted(clk.items())
+                            if k.startswith("gfx_") and isinstance(v.get("clk"), dict)
+                            and isinstance(v["clk"].get("value"), (int, float))])
+    except Exception as ex:                        # a tool missing or an unexpected format
+        err = f"{type(ex).__name__}: {ex}"[:120]
+    finally:
+        stop.set()
+        t.join()
+    vals = [v for smp in samples for v in smp]
+    return {"mhz_mean": round(float(np.mean(vals)), 1) if vals else None,
+            "mhz_min": min(vals) if vals else None, "mhz_max": max(vals) if vals else None,
+            "samples": len(samples), "xcds": len(samples[-1]) if samples else 0,
+            "source": "amd-smi metric --clock (gfx clocks of every XCD) while the step runs "
+                      "back to back", **({"error": err} if err else {})}
+
+
+def sha16(*arrays) -> str:
+    h = hashlib.sha256()
+    for a in arrays:
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()[:16]
+
+
 def dev_bf16(torch, bits: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
@@ -131,13 +200,20 @@ def cpu_baseline(w, inp, target_s: float) -> dict:
     wq, ws = o.quant_per_channel(inp.w_f32)        # offline weight prep, not timed
     rng = np.random.default_rng(w.seed)
 
+    parts = {"quant": 0.0, "gemm": 0.0, "epilogue": 0.0}
+
     def step(rows):
         t0 = time.perf_counter()
         xq, xs = o.quant_per_token(inp.x_bf16)
         t1 = time.perf_counter()
         acc = o.gemm_i32(xq, wq, rows)
+        t2 = time.perf_counter()
         o.epilogue_f32(acc, xs if rows is None else xs[rows], ws, inp.bias_bf16)
-        return t1 - t0, time.perf_counter() - t1
+        t3 = time.perf_counter()
+        parts["quant"] += t1 - t0
+        parts["gemm"] += t2 - t1
+        parts["epilogue"] += t3 - t2
+        return t1 - t0, t3 - t1
 
     xq, _ = o.quant_per_token(inp.x_bf16)
     probe = np.sort(rng.choice(w.M, min(w.M, 4), replace=False))
@@ -152,6 +228,7 @@ def cpu_baseline(w, inp, target_s: float) -> dict:
             t_sum += tq + tg
             reps += 1
         t_total = t_sum / reps
+        scale = 1.0
         sample = (f"{reps} full oracle steps (per-token quant of X [{w.M},{w.K}], exact int32 "
                   f"GEMM and fp32 epilogue on all rows), {t_sum:.1f} s measured, mean per step")
     else:
@@ -166,6 +243,9 @@ def cpu_baseline(w, inp, target_s: float) -> dict:
         sample = (f"{reps} x (full per-token quant of X [{w.M},{w.K}] plus exact int32 GEMM "
                   f"and fp32 epilogue on {n_rows} of {w.M} token rows, x{scale:.2f} to all "
                   f"rows); {tq_sum + tg_sum:.1f} s measured, mean per step")
+    t_quant = parts["quant"] / reps
+    t_gemm = parts["gemm"] * scale / reps
+    t_epi = parts["epilogue"] * scale / reps
     return {
         "value": round(w.ops / t_total / 1e12, 6),
         "unit": "TOP/s",
@@ -173,7 +253,28 @@ def cpu_baseline(w, inp, target_s: float) -> dict:
         "kind": "oracle",
         "sample": sample,
         "seconds_per_step": round(t_total, 4),
+        "cpu_model": cpu_model(),
+        "parts_per_full_step": {
+            "quant_s": sig4(t_quant), "quant_gbps": sig4((3 * w.M * w.K + 4 * w.M) / t_quant / 1e9),
+            "gemm_s": sig4(t_gemm), "gemm_gops": sig4(w.ops / t_gemm / 1e9),
+            "epilogue_s": sig4(t_epi),
+        },
     }
+
+
+def sig4(v: float) -> float:
+    return float(f"{v:.4g}")
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def copy_reference(torch, steps: int) -> dict:
@@ -283,6 +384,8 @@ def main(argv=None) -> int:
     ms_step2 = time_loop(torch, step_two_calls, args.steps)
     ms_mm = time_loop(torch, mm, args.steps)
     ms_quant = time_loop(torch, quant, args.steps)
+    each = {name: time_each(torch, fn, min(args.steps, 100))
+            for name, fn in (("step", step), ("mm", mm), ("quant", quant))}
 
     # Cold variant of the matmul: rotate over weight copies larger than the
     # 256 MB last-level cache so each launch streams its weight from HBM.
@@ -307,6 +410,10 @@ def main(argv=None) -> int:
                   "tops": round(2 * M * N * K / (vendor_ms * 1e-3) / 1e12, 2)}
     except Exception as ex:                        # not every shape is supported
         vendor = {"op": "torch._int_mm", "error": str(ex)[:160]}
+    inputs_sha = {"x_bf16": sha16(inp.x_bf16), "wq": sha16(wq.cpu().numpy()),
+                  "ws": sha16(ws.cpu().numpy()),
+                  "bias_bf16": None if inp.bias_bf16 is None else sha16(inp.bias_bf16),
+                  "digest": "first 16 hex of sha256 over the bytes"}
     del wq
 
     quant_bytes = 3 * M * K + 4 * M
@@ -331,14 +438,17 @@ def main(argv=None) -> int:
                    "step": "int8_quant_scaled_mm: per-token quant + scaled matmul (bf16 out), "
                            "one call"},
         "pct_mfma_peak_step": round(100 * mm_ops / (ms_step * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),
+        "step_us_isolated_median": each["step"][0], "step_us_isolated_min": each["step"][1],
         "step_two_calls": {"us": round(ms_step2 * 1e3, 3),
                            "tops": round(mm_ops / (ms_step2 * 1e-3) / 1e12, 2),
                            "calls": "int8_quant_per_token then int8_scaled_mm"},
         "scaled_mm": {"us": round(ms_mm * 1e3, 3), "tops": round(achieved, 2),
+                      "us_isolated_median": each["mm"][0], "us_isolated_min": each["mm"][1],
                       "us_cold": round(ms_mm_cold * 1e3, 3),
                       "tops_cold": round(mm_ops / (ms_mm_cold * 1e-3) / 1e12, 2),
                       "min_hbm_bytes": mm_min_bytes},
-        "quant": {"us": round(ms_quant * 1e3, 3),
+        "quant": {"us": round(ms_quant * 1e3, 3), "us_isolated_median": each["quant"][0],
+                  "us_isolated_min": each["quant"][1],
                   "gbps": round(quant_bytes / (ms_quant * 1e-3) / 1e9, 1),
                   "bytes": quant_bytes},
         "roofline": {
@@ -352,6 +462,8 @@ def main(argv=None) -> int:
         },
         "vendor_int8_gemm": vendor,
         "source_digest": source_digest(),
+        "inputs_sha256": inputs_sha,
+        "sclk_under_load": sclk_under_load(torch, step),
     }
 
     if not args.no_decode:
