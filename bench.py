@@ -52,11 +52,12 @@ def parse_args(argv=None):
                    help="skip the quant bandwidth run on the FFN-down activations")
     p.add_argument("--no-decode", action="store_true",
                    help="skip the one-token (decode) measurement of the fused-QKV layer")
-    p.add_argument("--only", choices=["step", "step2", "mm", "quant", "copy", "decode"],
+    p.add_argument("--only", choices=["step", "step2", "mm", "mm8", "quant", "copy", "decode"],
                    default=None,
                    help="launch only this part in a loop (for profiler runs); 'copy' is a "
                         "plain 256 MiB device copy kernel, the calibration for HBM byte "
-                        "counters; 'decode' is the one-token fused-QKV step")
+                        "counters; 'decode' is the one-token fused-QKV step; 'mm8' is the "
+                        "e4m3 twin's scaled matmul on the same layer")
     return p.parse_args(argv)
 
 
@@ -365,7 +366,15 @@ def main(argv=None) -> int:
         if args.only == "copy":
             copy_src = torch.ones((64 << 20,), dtype=torch.float32, device="cuda")
             copy_dst = torch.empty_like(copy_src)
-        fn = {"step": step, "step2": step_two_calls, "mm": mm, "quant": quant,
+        mm8 = None
+        if args.only == "mm8":
+            packed8, ws8 = ops.fp8_quant_prepack_weight(torch.from_numpy(inp.w_f32).cuda())
+            xq8, xs8 = ops.fp8_quant_per_token(x)
+            mm8 = Bound(L.fp8_scaled_mm_tile, xq8.data_ptr(), xq8.stride(0), xs8.data_ptr(),
+                        packed8.data_ptr(), ws8.data_ptr(),
+                        None if bias is None else bias.data_ptr(), M, N, K, 0, out.data_ptr(), N,
+                        stream, tile)
+        fn = {"step": step, "step2": step_two_calls, "mm": mm, "mm8": mm8, "quant": quant,
               "copy": lambda: torch.neg(copy_src, out=copy_dst)}[args.only]
         for _ in range(args.warmup + args.steps):
             fn()
