@@ -228,9 +228,11 @@ w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const float *x_
  * Requirements: those of int8_scaled_mm, plus ldx >= K, x 16-byte aligned
  * and ldx a multiple of 8; x_scale is required in both output modes.
  *
- * When the chosen tile is one of the main kernel's and every workgroup of
- * the matmul can be resident at once (true for the fused-QKV layer at M 512
- * and smaller), one launch does both steps: each workgroup quantizes a slice
+ * When the chosen tile is one of the main kernel's, every workgroup of the
+ * matmul can be resident at once (true for the fused-QKV layer at M 512
+ * and smaller) and xq and x_scale both start on 256-byte boundaries (so
+ * that no cache line holds rows of two row tiles; buffers from the usual
+ * allocators are), one launch does both steps: each workgroup quantizes a slice
  * of rows, raises its flag (a word in the library's device memory, set to a
  * number unique to the launch), and waits, bounded, only for the flags of
  * its own tile's rows; should a wait ever run out, that workgroup quantizes
@@ -247,8 +249,9 @@ w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const float *x_
  * first column block also write xq and x_scale. This form is safe under
  * graph capture.
  *
- * Otherwise (a grid too large to be resident, or more rows on a small-M
- * tile) the two steps run as two launches on `stream`.
+ * Otherwise (a grid too large to be resident, xq or x_scale not 256-byte
+ * aligned, or more rows on a small-M tile) the two steps run as two
+ * launches on `stream`.
  */
 w8a8_status_t int8_quant_scaled_mm(const uint16_t *x, int64_t ldx, int8_t *xq, int64_t ldq,
                                    float *x_scale, const void *w_packed, const float *w_scale,

@@ -443,6 +443,88 @@ def pin_fp8_quant(o):
     assert np.array_equal(qw, q) and np.array_equal(sw, s)
 
 
+def _torch_e4m3(v32: np.ndarray) -> np.ndarray:
+    """torch's float8_e4m3fn cast of fp32 values (round to nearest even), as codes."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(v32, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _fp8_rule(x32: np.ndarray):
+    """The FP8 quant rule written out with NumPy fp32 arithmetic and torch's
+    e4m3 cast: s = fl32(a/448), codes = e4m3_rne(clamp(fl32(x * fl32(448/a)), +-448))."""
+    a = np.abs(x32).max(axis=1)
+    live = a >= np.float32(2.0 ** -100)
+    s = np.where(live, a / np.float32(448), np.float32(0)).astype(np.float32)
+    inv = np.where(live, np.float32(448) / np.where(live, a, 1), 0).astype(np.float32)
+    t = np.clip((x32 * inv[:, None]).astype(np.float32), -448, 448).astype(np.float32)
+    q = _torch_e4m3(t)
+    q[~live] = 0
+    return q, s
+
+
+def _fp8_tie_rows(seed=35, rows=192):
+    """fp32 rows whose products x * fl32(448/a) land exactly on e4m3 rounding
+    ties. Element 0 is the absmax a (uniform in [1, 2), sign alternating);
+    the rest are the fp32 values nearest T / fl32(448/a), kept where the
+    product rounds back to exactly T, for ties T between neighbouring e4m3
+    values (normal and subnormal)."""
+    rng = np.random.default_rng(seed)
+    ties = np.array([1.0625, 1.1875, 0.53125, 3.375, 13.0, 0.02734375, 2.0 ** -10, 3 * 2.0 ** -10,
+                     -1.0625, -1.1875, -2.0 ** -10], np.float32)
+    out = []
+    while len(out) < rows:
+        a = np.float32(rng.uniform(1, 2))
+        inv = np.float32(448) / a
+        row = [a if len(out) % 2 == 0 else -a]
+        for T in ties:
+            x = np.float32(T / inv)
+            for cand in (x, np.nextafter(x, np.float32(np.inf)), np.nextafter(x, np.float32(-np.inf))):
+                if np.float32(cand * inv) == T and abs(cand) < a:
+                    row.append(cand)
+                    break
+        if len(row) > 6:
+            out.append(np.array(row + [np.float32(0)] * (len(ties) + 1 - len(row)), np.float32))
+    return np.stack(out)
+
+
+def pin_fp8_quant_exact(o):
+    """The FP8 quant rule exactly (page "Online Quantization", Parameters: FP8
+    with the dynamic activation scheme, read like the int8 rule with 448 in
+    place of 127): the scale is the correctly rounded fp32 quotient a/448 and
+    each code is torch's e4m3 (nearest-even) cast of fl32(x * fl32(448/a))
+    clamped to +-448; on hand-built rows whose products fall exactly on
+    ties, and on hand-checked codes."""
+    # hand-checked: a = 448 gives inv = 1 and s = 1, so the codes are the
+    # e4m3 roundings of x itself; 1.0625 is the tie between 1 (0x38) and
+    # 1.125 (0x39) -> even 0x38; 1.1875 between 1.125 and 1.25 -> 0x3A;
+    # 2^-10 between 0 and 2^-9 -> +0; 3*2^-10 between 2^-9 (0x01) and
+    # 2^-8 (0x02) -> 0x02; a = 224 gives inv = 2, s = 0.5.
+    x = np.array([[448, 1.0625, 1.1875, -1.0625, 2.0 ** -10, 3 * 2.0 ** -10, -2.0 ** -10, 240],
+                  [224, 0.53125, 0.59375, -0.53125, 2.0 ** -11, 3 * 2.0 ** -11, 0, -224]], np.float32)
+    want = np.array([[0x7E, 0x38, 0x3A, 0xB8, 0x00, 0x02, 0x80, 0x77],
+                     [0x7E, 0x38, 0x3A, 0xB8, 0x00, 0x02, 0x00, 0xFE]], np.uint8)
+    for q, s in (o.fp8_quant_per_channel(x), o.fp8_quant_per_token(wl.f32_to_bf16_bits(x))):
+        assert np.array_equal(s, np.array([1.0, 0.5], np.float32)), s
+        assert np.array_equal(q, want), q
+    # the rule on random rows (scale quotient, reciprocal product, cast)
+    rng = np.random.default_rng(36)
+    xr = (rng.standard_normal((64, 333)) * 10.0 ** rng.uniform(-6, 6, (64, 1))).astype(np.float32)
+    xr[5] = 0
+    xr[6] *= np.float32(2.0 ** -110)
+    for src, (q, s) in ((xr, o.fp8_quant_per_channel(xr)),
+                        (_f32(wl.f32_to_bf16_bits(xr)), o.fp8_quant_per_token(wl.f32_to_bf16_bits(xr)))):
+        qr, sr = _fp8_rule(src)
+        assert np.array_equal(s, sr)
+        assert np.array_equal(q, qr)
+    # products exactly on ties
+    xt = _fp8_tie_rows()
+    q, s = o.fp8_quant_per_channel(xt)
+    qr, sr = _fp8_rule(xt)
+    assert np.array_equal(s, sr)
+    assert np.array_equal(q, qr)
+
+
 def pin_fp8_gemm(o):
     rng = np.random.default_rng(33)
     codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
@@ -682,6 +764,6 @@ FAST_PINS = [pin_quant_ties, pin_quant_zero_rows, pin_quant_invariants, pin_gemm
              pin_gemm_numpy, pin_bf16_rounding, pin_epilogue_exact, pin_epilogue_order,
              pin_f16_conversions,
              pin_quant_f16, pin_epilogue_f16_exact, pin_e4m3_conversions, pin_fp8_quant,
-             pin_fp8_gemm, pin_fp8_epilogue, pin_layer_vs_numpy, pin_fused_qkv_stack]
+             pin_fp8_quant_exact, pin_fp8_gemm, pin_fp8_epilogue, pin_layer_vs_numpy, pin_fused_qkv_stack]
 PAGE_PINS = [pin_pages_rel_l2, pin_pages_missing_act_scale]
 ALL_PINS = FAST_PINS + PAGE_PINS

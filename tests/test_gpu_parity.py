@@ -7,9 +7,7 @@ fixed-order fp32 epilogue bit for bit.
 
 Sizes: small and mid shapes span several tiles with ragged M/N/K tails and
 run the oracle in full; the five workload shapes run at full size in the
-launch configuration the benchmark times, checked on sampled token rows
-(oracle row by row) plus exact int64 row- and column-sum identities of the
-accumulators over every row and column.
+launch configuration the benchmark times, every element compared.
 """
 from __future__ import annotations
 
@@ -327,53 +325,92 @@ def test_scaled_mm_empty_and_determinism(ops, orc):
 # ---------------------------------------------------------------------------
 # The five workloads at full size, in the benchmark's launch configuration
 # ---------------------------------------------------------------------------
-def _sample_rows(M, rng, n=40):
-    rows = set(rng.choice(M, min(M, n), replace=False).tolist())
-    rows |= {0, M - 1, (M - 1) // 2}
-    return np.array(sorted(rows), np.int64)
-
-
-@pytest.mark.parametrize("name", [w.name for w in wl.WORKLOADS])
-def test_workload_full_size(ops, orc, name):
-    w = wl.by_name(name)
+def full_size_parity(ops, orc, w) -> dict:
+    """Run workload w at full size through the product path (W8A8Linear: the
+    per-token quant and scaled matmul in one call) and compare every element
+    with the oracle: codes, token and channel scales, the unpacked weight,
+    the int32 accumulators (I32 mode) and the bf16 outputs (against the
+    fp32 epilogue bit for bit and the fp64 epilogue within the tolerance
+    bar). Also the rel-L2 of the outputs against fp64 matmuls of the
+    dequantized operands (the pages' 0.17 % statistic) and of the raw bf16 X
+    and fp32 W. Returns the counts; the caller asserts."""
     inp = wl.generate(w)
     from w8a8_int8_dynamic_amd import W8A8Linear
     layer = W8A8Linear.from_float(torch.from_numpy(inp.w_f32).to(DEV),
                                   None if inp.bias_bf16 is None else bf16_dev(inp.bias_bf16))
     x_d = bf16_dev(inp.x_bf16)
     out = layer(x_d)
+    xq, xs = ops.quant_per_token(x_d)
+    acc = ops.scaled_mm(xq, None, layer.w_packed, None, w.N, out_dtype=torch.int32)
     torch.cuda.synchronize()
     assert out.shape == (w.M, w.N) and out.dtype == torch.bfloat16
-    # operands, bit-exact
+    r = {"name": w.name, "shape": (w.M, w.K, w.N)}
     wq_ref, ws_ref = orc.quant_per_channel(inp.w_f32)
-    assert np.array_equal(layer.w_scale.cpu().numpy(), ws_ref)
-    assert np.array_equal(ops.unpack_weight(layer.w_packed, w.N, w.K).cpu().numpy(), wq_ref)
-    xq, xs = ops.quant_per_token(x_d)
     xq_ref, xs_ref = orc.quant_per_token(inp.x_bf16)
-    assert np.array_equal(xq.cpu().numpy(), xq_ref) and np.array_equal(xs.cpu().numpy(), xs_ref)
-    # accumulators: sampled rows exactly, and exact row/column sums of every row and column
-    acc = ops.scaled_mm(xq, None, layer.w_packed, None, w.N, out_dtype=torch.int32).cpu().numpy()
-    rows = _sample_rows(w.M, np.random.default_rng(w.seed))
-    acc_ref = orc.gemm_i32(xq_ref, wq_ref, rows)
-    assert np.array_equal(acc[rows], acc_ref)
-    xq64, wq64 = xq_ref.astype(np.int64), wq_ref.astype(np.int64)
-    assert np.array_equal(acc.sum(axis=1, dtype=np.int64), xq64 @ wq64.sum(axis=0))
-    assert np.array_equal(acc.sum(axis=0, dtype=np.int64), xq64.sum(axis=0) @ wq64.T)
-    # outputs on the sampled rows
-    got = bits_np(out)[rows]
-    ref32 = orc.epilogue_f32(acc_ref, xs_ref[rows], ws_ref, inp.bias_bf16)
-    ref64 = orc.epilogue_f64(acc_ref, xs_ref[rows], ws_ref, inp.bias_bf16)
-    exact = check_out(got, ref32, ref64, name)
-    assert exact == 1.0, f"{name}: {exact:.6f} bit-exact"
-    # every output finite; bf16 rounding vs fp64 on the dequantized operands ~0.17 %
-    assert torch.isfinite(out.float()).all()
-    deq = (xq_ref[rows].astype(np.float64) * xs_ref[rows, None].astype(np.float64)) @ \
-          (wq_ref.astype(np.float64) * ws_ref[:, None].astype(np.float64)).T
-    if inp.bias_bf16 is not None:
-        deq += f64(inp.bias_bf16)[None, :]
-    rel = np.linalg.norm(f64(got) - deq) / np.linalg.norm(deq)
-    print(f"\n{name}: rel-L2 vs fp64 dequantized reference {100 * rel:.4f} %")
-    assert rel < 0.0025
+    r["ws_equal"] = int((layer.w_scale.cpu().numpy() == ws_ref).sum())
+    r["wq_equal"] = int((ops.unpack_weight(layer.w_packed, w.N, w.K).cpu().numpy() == wq_ref).sum())
+    r["xs_equal"] = int((xs.cpu().numpy() == xs_ref).sum())
+    r["xq_equal"] = int((xq.cpu().numpy() == xq_ref).sum())
+    acc_ref = orc.gemm_i32(xq_ref, wq_ref)
+    r["acc_equal"] = int((acc.cpu().numpy() == acc_ref).sum())
+    del acc
+    got = bits_np(out)
+    del out
+    ref32 = orc.epilogue_f32(acc_ref, xs_ref, ws_ref, inp.bias_bf16)
+    ref64 = orc.epilogue_f64(acc_ref, xs_ref, ws_ref, inp.bias_bf16)
+    del acc_ref
+    r["out_equal_f32_epilogue"] = int((got == ref32).sum())
+    g, ref = f64(got), f64(ref64)
+    rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+    r["finite"] = bool(np.all(np.isfinite(g)))
+    r["outside_tolerance"] = int((np.abs(g - ref) > RTOL * np.abs(ref) + ATOL_RMS * rms).sum())
+    nz = ref != 0
+    r["max_rel_vs_f64_epilogue"] = float(np.max(np.abs(g - ref)[nz] / np.abs(ref)[nz]))
+    r["rel_l2_vs_f64_epilogue"] = float(np.linalg.norm(g - ref) / np.linalg.norm(ref))
+    del ref, ref32, ref64
+    b64 = 0.0 if inp.bias_bf16 is None else f64(inp.bias_bf16)[None, :]
+    deq = (xq_ref.astype(np.float64) * xs_ref.astype(np.float64)[:, None]) @ \
+          (wq_ref.astype(np.float64) * ws_ref.astype(np.float64)[:, None]).T + b64
+    r["rel_l2_vs_f64_dequantized"] = float(np.linalg.norm(g - deq) / np.linalg.norm(deq))
+    del deq
+    raw = f64(inp.x_bf16) @ inp.w_f32.astype(np.float64).T + b64
+    r["rel_l2_vs_f64_raw"] = float(np.linalg.norm(g - raw) / np.linalg.norm(raw))
+    return r
+
+
+def parity_table_row(r: dict) -> str:
+    M, K, N = r["shape"]
+    return (f"| {r['name']} | {M} x {K} x {N} | {r['xq_equal']:,} / {M * K:,} | "
+            f"{r['xs_equal'] + r['ws_equal']:,} / {M + N:,} | {r['wq_equal']:,} / {N * K:,} | "
+            f"{r['acc_equal']:,} / {M * N:,} | {r['out_equal_f32_epilogue']:,} / {M * N:,} | "
+            f"{r['outside_tolerance']} | {r['max_rel_vs_f64_epilogue']:.2e} | "
+            f"{100 * r['rel_l2_vs_f64_epilogue']:.4f} % | "
+            f"{100 * r['rel_l2_vs_f64_dequantized']:.3f} % | {100 * r['rel_l2_vs_f64_raw']:.2f} % |")
+
+
+PARITY_TABLE_HEAD = (
+    "| workload | M x K x N | codes equal | scales equal (xs, ws) | weight codes equal | "
+    "int32 acc equal | bf16 out equal to fp32 epilogue | outside tolerance | "
+    "max rel err vs fp64 epilogue | rel-L2 vs fp64 epilogue | rel-L2 vs fp64 dequantized "
+    "matmul | rel-L2 vs fp64 raw X W |\n|---|---|---|---|---|---|---|---|---|---|---|---|")
+
+
+@pytest.mark.parametrize("name", [w.name for w in wl.WORKLOADS])
+def test_workload_full_size(ops, orc, name):
+    """Every element of every workload at full size, bit-exact (codes,
+    scales, weight codes, int32 accumulators, bf16 outputs against the fp32
+    epilogue) and within the tolerance bar of the fp64 epilogue."""
+    w = wl.by_name(name)
+    r = full_size_parity(ops, orc, w)
+    print("\n" + parity_table_row(r))
+    M, K, N = r["shape"]
+    assert r["xq_equal"] == M * K and r["xs_equal"] == M
+    assert r["wq_equal"] == N * K and r["ws_equal"] == N
+    assert r["acc_equal"] == M * N
+    assert r["finite"] and r["outside_tolerance"] == 0
+    assert r["out_equal_f32_epilogue"] == M * N
+    # bf16 rounding against fp64 on the dequantized operands: ~0.17 %
+    assert r["rel_l2_vs_f64_dequantized"] < 0.0025
 
 
 # ---------------------------------------------------------------------------
@@ -638,6 +675,51 @@ def test_quant_scaled_mm_own_rows_path(ops, orc):
             assert torch.equal(out8.view(torch.int16), ref.view(torch.int16)), ops.tile_name(t)
     finally:
         L.w8a8_fused_wait_limit(prev)
+
+
+@pytest.mark.parametrize("q_off,s_off", [(16, 1), (0, 1), (16, 0), (256, 64), (48, 3)])
+def test_quant_scaled_mm_offset_code_and_scale_views(ops, orc, q_off, s_off):
+    """Codes and scales written into views that start inside a larger buffer
+    (xq at q_off bytes, xs at s_off floats): rows of two row tiles can then
+    share a cache line, which the one-launch path must not depend on (it is
+    taken only for 256-byte aligned buffers). Every main tile, int8 and
+    e4m3, against the oracle; the bytes around the views stay untouched."""
+    M, N, K = 384, 1536, 1040
+    inp = wl.random_case(M, K, N, 9650 + q_off + s_off, bias=True)
+    wq_ref, ws_ref = orc.quant_per_channel(inp.w_f32)
+    xq_ref, xs_ref = orc.quant_per_token(inp.x_bf16)
+    ref32 = orc.epilogue_f32(orc.gemm_i32(xq_ref, wq_ref), xs_ref, ws_ref, inp.bias_bf16)
+    packed = ops.prepack_weight(torch.from_numpy(wq_ref).to(DEV))
+    ws, x, b = torch.from_numpy(ws_ref).to(DEV), bf16_dev(inp.x_bf16), bf16_dev(inp.bias_bf16)
+    ldq = 1056                                      # a multiple of 16, not of 128
+    qbuf = torch.full((M * ldq + q_off + 64,), 0x5A, dtype=torch.int8, device=DEV)
+    sbuf = torch.full((M + s_off + 16,), -7.0, dtype=torch.float32, device=DEV)
+    xq = qbuf[q_off:q_off + M * ldq].view(M, ldq)[:, :K]
+    xs = sbuf[s_off:s_off + M]
+    main = [t for t in range(ops.tile_count()) if not ops.tile_name(t).startswith("s")]
+    for t in main:
+        qbuf.fill_(0x5A)
+        sbuf.fill_(-7.0)
+        out, _, _ = ops.quant_scaled_mm(x, packed, ws, N, b, tile=t, xq=xq, xs=xs)
+        torch.cuda.synchronize()
+        name = f"{ops.tile_name(t)} q_off {q_off} s_off {s_off}"
+        assert np.array_equal(xq.cpu().numpy(), xq_ref), name
+        assert np.array_equal(xs.cpu().numpy(), xs_ref), name
+        assert np.array_equal(bits_np(out), ref32), name
+        qh = qbuf.cpu().numpy()
+        assert np.all(qh[:q_off] == 0x5A) and np.all(qh[q_off + M * ldq:] == 0x5A), name
+        assert np.all(qh[q_off:q_off + M * ldq].reshape(M, ldq)[:, K:] == 0x5A), name
+        sh = sbuf.cpu().numpy()
+        assert np.all(sh[:s_off] == -7.0) and np.all(sh[s_off + M:] == -7.0), name
+    packed8, ws8 = ops.fp8_quant_prepack_weight(torch.from_numpy(inp.w_f32).to(DEV))
+    q8buf = torch.zeros((M * ldq + q_off + 64,), dtype=torch.uint8, device=DEV)
+    xq8 = q8buf[q_off:q_off + M * ldq].view(M, ldq)[:, :K]
+    for t in main:
+        ref8, rq8, rs8 = ops.fp8_quant_scaled_mm(x, packed8, ws8, N, b, tile=t)
+        out8, q8, s8 = ops.fp8_quant_scaled_mm(x, packed8, ws8, N, b, tile=t, xq=xq8, xs=xs)
+        torch.cuda.synchronize()
+        assert torch.equal(q8, rq8) and torch.equal(s8, rs8), ops.tile_name(t)
+        assert torch.equal(out8.view(torch.int16), ref8.view(torch.int16)), ops.tile_name(t)
 
 
 def test_quant_scaled_mm_overlapping_streams(ops, orc):

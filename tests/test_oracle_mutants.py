@@ -60,6 +60,8 @@ MUTANTS = {
     "fp8_underflow_loses_sign": ("if (r == 0.0)\n        return sign;", "if (r == 0.0)\n        return 0;"),
     "fp8_exponent_bias_8": ("((exp_unbiased + 7) << 3)", "((exp_unbiased + 8) << 3)"),
     "fp8_subnormal_boundary": ("if (exp_unbiased < -6)", "if (exp_unbiased < -7)"),
+    "fp8_scale_by_reciprocal": ("float s = a / 448.0f;", "float s = a * (1.0f / 448.0f);"),
+    "fp8_codes_by_divide": ("float t = v[k] * inv;\n        if (t > 448.0f)", "float t = v[k] / s;\n        if (t > 448.0f)"),
     "fp8_no_zero_row_rule": ("if (a < 0x1p-100f) {\n        *scale = 0.0f;\n        for (int64_t k = 0; k < K; ++k)\n            q[k] = 0;\n        return;\n    }\n    float s = a / 448.0f;",
                              "if (a < 0.0f) {\n        *scale = 0.0f;\n        for (int64_t k = 0; k < K; ++k)\n            q[k] = 0;\n        return;\n    }\n    float s = a / 448.0f;"),
 }

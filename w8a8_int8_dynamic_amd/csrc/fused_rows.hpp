@@ -21,7 +21,9 @@
 // stores, coherent across the XCDs once complete, so no write-back of the
 // producer's L2 is needed before the flag goes up. No cache of a consumer's
 // CU or XCD can hold an older copy of the rows: caches start each launch
-// clean and no workgroup reads a tile's rows before its wait.
+// clean, no workgroup reads a tile's rows before its wait, and the host
+// takes this path only when the codes and scales buffers are aligned so
+// that no cache line holds rows of two row tiles (kFusedAlign).
 #pragma once
 
 #include <type_traits>
@@ -44,6 +46,10 @@ static __device__ unsigned g_flag[kMaxProducers];
 // MmArgs::wait_limit, which the host can lower (0 makes every workgroup take
 // its own-rows path at once, which tests use).
 constexpr unsigned kDefaultWaitLimit = 1u << 12;
+
+// Alignment (bytes) that the codes and scales buffers need for the
+// one-launch path: at least a cache line (128 bytes on gfx950), with margin.
+constexpr uintptr_t kFusedAlign = 256;
 
 // Short rows (K <= 64 * 8 * CPL): one wavefront per row, CPL 16-byte chunks
 // per lane, 8 / CPL rows per wavefront in flight (all their loads issued

@@ -155,6 +155,17 @@ hipError_t launch_quant_scaled_mm_entry(MmArgs a, int mode, const TileEntry &e, 
         rpw *= 2;
     if (e.bm % rpw != 0 || ceil_div(a.M, rpw) > fused::kMaxProducers)
         return hipErrorNotSupported;
+    // Consumers read the codes and scales of their own row tile with plain
+    // loads once its producers have published, with no cache invalidation.
+    // That is only sound when no cache line holds rows of two row tiles: a
+    // consumer could otherwise pull in (and its XCD's L2 keep) a line whose
+    // other part a later producer still has to write. A row tile's codes
+    // span BM * ldq bytes (a multiple of 1024) and its scales BM * 4 (a
+    // multiple of 256), so bases aligned to kFusedAlign keep every tile on
+    // whole lines; other buffers take the two launches.
+    if (reinterpret_cast<uintptr_t>(a.xq) % fused::kFusedAlign != 0 ||
+        reinterpret_cast<uintptr_t>(a.xs) % fused::kFusedAlign != 0)
+        return hipErrorNotSupported;
     // The flags carry an epoch fixed when the launch is made. A captured graph
     // would replay one epoch forever, and a replay could then take the flags
     // its predecessor raised for its own rows; so under stream capture the
