@@ -50,6 +50,10 @@ def parse_args(argv=None):
                    help="target wall time of the oracle's sampled GEMM")
     p.add_argument("--no-quant-large", action="store_true",
                    help="skip the quant bandwidth run on the FFN-down activations")
+    p.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV", default=None,
+                   help="print the summary of a rocprofv3 kernel trace of a bench run (no GPU)")
+    p.add_argument("--no-workloads", action="store_true",
+                   help="skip the per-workload GPU and oracle records and the accuracy record")
     p.add_argument("--no-decode", action="store_true",
                    help="skip the one-token (decode) measurement of the fused-QKV layer")
     p.add_argument("--only", choices=["step", "step2", "mm", "mm8", "quant", "copy", "decode"],
@@ -306,8 +310,189 @@ def traffic_record(kernel: str, workload: str):
     return entry.get("bytes_per_launch")
 
 
+def omp_threads(n=None) -> int:
+    """OpenMP threads of the oracle's parallel regions started from this
+    thread: set to n when given; returns the current maximum."""
+    gomp = ctypes.CDLL("libgomp.so.1")
+    if n is not None:
+        gomp.omp_set_num_threads(int(n))
+    return int(gomp.omp_get_max_threads())
+
+
+def workload_records(torch, L, ops, wl, steps: int) -> dict:
+    """Every workload at full size on the GPU: the step (int8_quant_scaled_mm,
+    one call), the two separate calls, int8_scaled_mm alone and the per-token
+    quant alone, each as the mean of back-to-back launches from HIP events on
+    the launch stream, with TOP/s and the fraction of the int8 MFMA peak
+    (matmul) or of HBM (quant). Inputs are resident in HBM; for the two
+    largest workloads the whole set fits the 256 MB last-level cache only in
+    part, so these are the figures of an ordinary layer call."""
+    recs = {}
+    stream = torch.cuda.current_stream().cuda_stream
+    for w in wl.WORKLOADS:
+        M, K, N = w.M, w.K, w.N
+        inp = wl.generate(w)
+        x = dev_bf16(torch, inp.x_bf16)
+        bias = None if inp.bias_bf16 is None else dev_bf16(torch, inp.bias_bf16)
+        packed, ws = ops.quant_prepack_weight(torch.from_numpy(inp.w_f32).cuda())
+        xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        xs = torch.empty((M,), dtype=torch.float32, device="cuda")
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        bp = None if bias is None else bias.data_ptr()
+        tile = ops.tile_auto(M, N, K)
+        quant = Bound(L.int8_quant_per_token, x.data_ptr(), M, K, K, xq.data_ptr(), K,
+                      xs.data_ptr(), stream)
+        step = Bound(L.int8_quant_scaled_mm, x.data_ptr(), K, xq.data_ptr(), K, xs.data_ptr(),
+                     packed.data_ptr(), ws.data_ptr(), bp, M, N, K, 0, out.data_ptr(), N, stream)
+        mm = Bound(L.int8_scaled_mm, xq.data_ptr(), K, xs.data_ptr(), packed.data_ptr(),
+                   ws.data_ptr(), bp, M, N, K, 0, out.data_ptr(), N, stream)
+
+        def two():
+            quant()
+            mm()
+
+        iters = max(10, min(steps, int(20000 / max(1.0, w.ops / 2.0e9))))
+        settle(torch, step, 0.15)
+        t_step = time_loop(torch, step, iters)
+        t_two = time_loop(torch, two, iters)
+        t_mm = time_loop(torch, mm, iters)
+        t_q = time_loop(torch, quant, iters)
+        qbytes = 3 * M * K + 4 * M
+        tops = w.ops / (t_mm * 1e-3) / 1e12
+        recs[w.name] = {
+            "M": M, "K": K, "N": N, "tile": ops.tile_name(tile), "launches": iters,
+            "step_us": round(t_step * 1e3, 3),
+            "step_tops": round(w.ops / (t_step * 1e-3) / 1e12, 1),
+            "two_calls_us": round(t_two * 1e3, 3),
+            "scaled_mm_us": round(t_mm * 1e3, 3), "scaled_mm_tops": round(tops, 1),
+            "scaled_mm_frac_mfma_peak": round(tops / PEAK_INT8_TOPS, 4),
+            "quant_us": round(t_q * 1e3, 3),
+            "quant_gbps": round(qbytes / (t_q * 1e-3) / 1e9, 1),
+            "quant_frac_hbm_peak": round(qbytes / (t_q * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        }
+        del x, bias, packed, ws, xq, xs, out
+        torch.cuda.empty_cache()
+    return recs
+
+
+def oracle_records(wl, target_s: float = 2.5) -> dict:
+    """The oracle on every workload, on all host cores and (for the three
+    smaller workloads) on one core: per-token quant of all rows, then the
+    exact int32 GEMM and fp32 epilogue on a sample of token rows sized to
+    about target_s seconds, scaled to all rows (all rows when a full step is
+    shorter). int8 TOP/s of 2*M*N*K per full step."""
+    import oracle
+    o = oracle.load()
+    full = omp_threads()
+    recs = {"build_flags": " ".join(oracle.CFLAGS), "cpu_model": cpu_model(),
+            "threads_all": full}
+    for w in wl.WORKLOADS:
+        inp = wl.generate(w)
+        wq, ws = o.quant_per_channel(inp.w_f32)
+        rng = np.random.default_rng(w.seed + 77)
+        rec = {}
+        for label, threads in (("all_cores", full), ("one_core", 1)):
+            if label == "one_core" and w.name not in ("tiny", "attn_out", "fused_qkv"):
+                continue
+            omp_threads(threads)
+            t0 = time.perf_counter()
+            xq, xs = o.quant_per_token(inp.x_bf16)
+            tq = time.perf_counter() - t0
+            probe = np.sort(rng.choice(w.M, min(w.M, 2), replace=False))
+            t0 = time.perf_counter()
+            o.gemm_i32(xq, wq, probe)
+            per_row = (time.perf_counter() - t0) / len(probe)
+            n_rows = int(min(w.M, max(2, target_s / max(per_row, 1e-9))))
+            rows = None if n_rows >= w.M else np.sort(rng.choice(w.M, n_rows, replace=False))
+            t0 = time.perf_counter()
+            acc = o.gemm_i32(xq, wq, rows)
+            o.epilogue_f32(acc, xs if rows is None else xs[rows], ws, inp.bias_bf16)
+            tg = (time.perf_counter() - t0) * (w.M / (w.M if rows is None else n_rows))
+            rec[label] = {"threads": threads, "seconds_per_step": sig4(tq + tg),
+                          "tops": sig4(w.ops / (tq + tg) / 1e12),
+                          "quant_gbps": sig4((3 * w.M * w.K + 4 * w.M) / tq / 1e9),
+                          "rows_timed": w.M if rows is None else n_rows}
+        omp_threads(full)
+        recs[w.name] = rec
+    return recs
+
+
+def accuracy_record(torch, ops, wl) -> dict:
+    """Rel-L2 of the fused-QKV layer's bf16 output (the product path, every
+    element) against fp32 matmuls (NumPy float32 GEMM) of the dequantized
+    operands (xq*xs)(wq*ws)^T and of the raw bf16 X and fp32 W, next to the
+    0.17 % the pages report for their raw-op check against a float32
+    reference. The first is the bf16 output rounding (plus the fp32
+    reference's own rounding); the second adds the quantization error."""
+    w = wl.by_name("fused_qkv")
+    inp = wl.generate(w)
+    from w8a8_int8_dynamic_amd import W8A8Linear
+    layer = W8A8Linear.from_float(torch.from_numpy(inp.w_f32).cuda())
+    x = dev_bf16(torch, inp.x_bf16)
+    out = layer(x)
+    xq, xs = ops.quant_per_token(x)
+    wq = ops.unpack_weight(layer.w_packed, w.N, w.K)
+    g = out.float().cpu().numpy().astype(np.float64)
+    a = (xq.cpu().numpy().astype(np.float32) * xs.cpu().numpy()[:, None])
+    b = (wq.cpu().numpy().astype(np.float32) * layer.w_scale.cpu().numpy()[:, None])
+    deq = (a @ b.T).astype(np.float64)
+    raw = (wl.bf16_bits_to_f32(inp.x_bf16) @ inp.w_f32.T).astype(np.float64)
+
+    def rel(r):
+        return float(np.linalg.norm(g - r) / np.linalg.norm(r))
+
+    return {"workload": w.description,
+            "rel_l2_vs_fp32_dequantized_matmul_pct": round(100 * rel(deq), 4),
+            "rel_l2_vs_fp32_raw_matmul_pct": round(100 * rel(raw), 3),
+            "pages_rel_l2_pct": 0.17,
+            "reading": "the pages' figure is read as the bf16 rounding of the output against "
+                       "a float32 matmul of the dequantized operands"}
+
+
+def trace_summary(path: str) -> str:
+    """Summary of a rocprofv3 kernel trace (its kernel_trace.csv) of a bench
+    run: per kernel, the dispatch count and mean / min / max duration, over
+    the whole run and over the timed step loop alone (the dispatches between
+    the two bitwise_not marker launches that bracket it), with the loop's
+    start-to-start period. Markdown text."""
+    import csv
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    marks = [i for i, r in enumerate(rows) if "bitwise_not" in r["Kernel_Name"]]
+
+    def short(name: str) -> str:
+        name = name.replace("(anonymous namespace)::", "").replace("w8a8::", "")
+        return name.split("(")[0].replace("void ", "")
+
+    def table(sel, title):
+        by = {}
+        for r in sel:
+            by.setdefault(short(r["Kernel_Name"]), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        out = [f"{title}", "", "| kernel | dispatches | mean us | min us | max us |",
+               "|---|---|---|---|---|"]
+        for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+            out.append(f"| `{k}` | {len(v)} | {np.mean(v):.3f} | {min(v):.3f} | {max(v):.3f} |")
+        return out
+
+    lines = table(rows, "All dispatches of the run:")
+    if len(marks) >= 2:
+        loop = rows[marks[0] + 1:marks[1]]
+        starts = [int(r["Start_Timestamp"]) for r in loop]
+        ends = [int(r["End_Timestamp"]) for r in loop]
+        lines += [""] + table(loop, "The timed step loop (between the markers):")
+        if len(loop) > 1:
+            lines += ["", f"Timed step loop: {len(loop)} dispatches, first start to last end "
+                          f"{(ends[-1] - starts[0]) / 1e3:.3f} us, "
+                          f"{(ends[-1] - starts[0]) / 1e3 / len(loop):.3f} us per dispatch; mean "
+                          f"start-to-start period {(starts[-1] - starts[0]) / 1e3 / (len(loop) - 1):.3f} us."]
+    return "\n".join(lines)
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return 0
     if args.gpus != 1 or world_size() != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
               f"{world_size()}); this build has no multi-GPU path.", file=sys.stderr)
@@ -389,7 +574,12 @@ def main(argv=None) -> int:
         step()
     torch.cuda.synchronize()
     settle(torch, step)
+    # Two launches of a kernel used nowhere else bracket the timed step loop,
+    # so a kernel trace of this run can pick out exactly its dispatches.
+    marker = torch.zeros((7,), dtype=torch.int16, device="cuda")
+    torch.bitwise_not(marker, out=marker)
     ms_step = time_loop(torch, step, args.steps)
+    torch.bitwise_not(marker, out=marker)
     ms_step2 = time_loop(torch, step_two_calls, args.steps)
     ms_mm = time_loop(torch, mm, args.steps)
     ms_quant = time_loop(torch, quant, args.steps)
@@ -482,8 +672,14 @@ def main(argv=None) -> int:
         rec["hbm_copy_reference"] = copy_reference(torch, args.steps)
     del x, xq, xs, out, packed
     torch.cuda.empty_cache()
+    if not args.no_workloads:
+        rec["workloads"] = workload_records(torch, L, ops, wl, args.steps)
+        rec["accuracy"] = accuracy_record(torch, ops, wl)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+        rec["cpu_baseline"]["build_flags"] = " ".join(__import__("oracle").CFLAGS)
+        if not args.no_workloads:
+            rec["oracle_workloads"] = oracle_records(wl)
     print(json.dumps(rec), flush=True)
     return 0
 
