@@ -152,35 +152,46 @@ constexpr int clcm(int a, int b) { return a / cgcd(a, b) * b; }
 
 // BM x BN output tile; WM row groups x WN column groups x WK k-groups of
 // wavefronts; token rows fetched LT stages ahead of their LDS write, weights
-// LW stages ahead of their use.
-template <int BM_, int BN_, int WM_, int WN_, int WK_, int LT_, int LW_>
+// LW stages ahead of their use. WL: the weights go through LDS as well (in
+// the token pipeline, LT stages ahead of their LDS write), so that row
+// groups sharing a weight fragment (WM = 2) fetch it once; LW is then
+// unused.
+template <int BM_, int BN_, int WM_, int WN_, int WK_, int LT_, int LW_, bool WL_ = false>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, WK = WK_, LT = LT_, LW = LW_;
+    static constexpr bool WLDS = WL_;
     static constexpr int NW = WM * WN * WK;            // wavefronts per workgroup
     static constexpr int THREADS = NW * 64;
     static constexpr int MB = BM / 16;                 // 16-row token images per k-block
     static constexpr int FM = BM / WM / 32;            // 32x32 MFMA tiles per wave, rows
     static constexpr int FN = BN / WN / 32;            // ... and columns
     static constexpr int AIMG = WK * MB;               // token images per stage
+    static constexpr int WIMG = WLDS ? WK * (BN / 16) : 0;  // weight images per stage in LDS
     static constexpr int LA = AIMG / NW;               // token loads per wave per stage
-    static constexpr int LB = 2 * FN;                  // weight loads per wave per stage
+    static constexpr int LW8 = WIMG / NW;              // weight image loads per wave (LDS path)
+    static constexpr int LB = WLDS ? LW8 : 2 * FN;     // weight loads per wave per stage
     static constexpr int LPW = LA + LB;                // global loads per wave per stage
     static constexpr int NA = LT;                      // token staging register sets
-    static constexpr int NB = LW + 1;                  // weight register sets
+    static constexpr int NB = WLDS ? 1 : LW + 1;       // weight register sets
     static constexpr int GROUP = clcm(clcm(NA, NB), 2);     // steps per unrolled loop body
-    static constexpr int AHEAD = cmax(LT + 2, LW);     // furthest stage a step fetches
+    static constexpr int AHEAD = WLDS ? LT + 2 : cmax(LT + 2, LW);  // furthest stage fetched
     // Steady-state wait at the top of a step: the token rows to be written
     // to LDS (fetched LT steps earlier, first in their step) and the weights
     // of this step (fetched LW steps earlier, last in their step) have landed.
-    static constexpr int VM = cmax(0, LB + (LT - 1) * LPW < (LW - 1) * LPW ? LB + (LT - 1) * LPW
-                                                                           : (LW - 1) * LPW);
-    static constexpr int STAGE = AIMG * 64;            // 16-byte slots per LDS stage
+    // Through LDS, the weights of stage s+2 come right after its tokens.
+    static constexpr int VM = WLDS ? (LT - 1) * LPW
+                                   : cmax(0, LB + (LT - 1) * LPW < (LW - 1) * LPW
+                                                 ? LB + (LT - 1) * LPW
+                                                 : (LW - 1) * LPW);
+    static constexpr int STAGE = (AIMG + WIMG) * 64;   // 16-byte slots per LDS stage
     static constexpr int RING = 2 * STAGE * 16;        // two LDS stages, bytes
     static constexpr int PART = (WK - 1) * BM * BN * 4;     // k-group partial sums
     static constexpr int PITCH = BN * 2 + 16;          // staged bf16 row, bytes
     static constexpr int OUTB = BM * PITCH;
-    static constexpr int TILE_OFF = cmax(RING, PART);  // bf16 tile after ring / partials
-    static constexpr int MAIN = TILE_OFF + OUTB;
+    // The bf16 tile goes after the k-group partials (which it meets in the
+    // epilogue); with one k-group it reuses the ring, idle by then.
+    static constexpr int TILE_OFF = WK > 1 ? cmax(RING, PART) : 0;
+    static constexpr int MAIN = cmax(TILE_OFF + OUTB, RING);
     static constexpr int SIDE = 2 * BN + BM;           // fp32 ws, bias, xs of the tile
     static constexpr int SIDE_PER_THREAD = (SIDE + THREADS - 1) / THREADS;
     static constexpr int FLAG = MAIN + SIDE * 4;        // one word: fused-path decision
@@ -188,6 +199,7 @@ struct Tile {
     static_assert(NW == 4 || NW == 8, "four or eight wavefronts per workgroup");
     static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "tile/wave mismatch");
     static_assert(AIMG % NW == 0, "token loads must split evenly over waves");
+    static_assert(WIMG % NW == 0, "weight image loads must split evenly over waves");
     static_assert(LT >= 2 && LW >= LT, "token lead >= 2, weight lead >= token lead");
     static_assert(VM < 64 && (LW + LT) * LPW < 64, "vmcnt range");
     static_assert(LDS <= 160 * 1024, "LDS budget");
@@ -300,9 +312,11 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
 #pragma unroll
         for (int i = 0; i < T::FM; ++i)
             acc[j][i] = Acc{};
-    v4i bq[T::NB][T::FN][2];                           // weight operand ring
+    v4i bq[T::NB][T::FN][2];                           // weight operand ring (direct path)
     v4i ast[T::NA][T::LA];                             // token staging ring
+    v4i bst[T::NA][T::LW8 > 0 ? T::LW8 : 1];           // weight image staging ring (LDS path)
     v4i xf[2][T::FM][2];                               // token operands, this and next stage
+    v4i bf[T::WLDS ? 2 : 1][T::FN][2];                 // weight operands from LDS, this and next
 
     // Global loads: token rows of stage t into staging set t % NA; weights of
     // stage t into ring set t % NB. Addresses are clamped into the operands,
@@ -322,12 +336,42 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
             for (int h = 0; h < 2; ++h)
                 bset[j][h] = bsrc[j][(int64_t)kb * 64 + h * 32];
     };
-    // Token rows of stage t from staging registers into LDS stage t % 2.
-    auto store = [&](int t, const v4i (&aset)[T::LA]) __attribute__((always_inline)) {
+    // LDS path: whole 1 KB weight images of stage t (image g = i*NW + wave of
+    // the stage is k-block g / (BN/16), channel image g % (BN/16) of the
+    // tile), one coalesced 16-byte load per lane.
+    auto load_w = [&](int t, v4i (&wset)[T::LW8 > 0 ? T::LW8 : 1]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < T::LW8; ++i) {
+            const int g = i * T::NW + wave;
+            const int kb = min(t * T::WK + g / (T::BN / 16), kblast);
+            const int img = min(n0 / 16 + g % (T::BN / 16), a.nblocks - 1);
+            wset[i] = reinterpret_cast<const v4i *>(a.wp)[((int64_t)img * a.kblocks + kb) * 64 + lane];
+        }
+    };
+    // Token rows (and, on the LDS path, weight images) of stage t from
+    // staging registers into LDS stage t % 2.
+    auto store = [&](int t, const v4i (&aset)[T::LA], const v4i (&wset)[T::LW8 > 0 ? T::LW8 : 1])
+                     __attribute__((always_inline)) {
         v4i *st = reinterpret_cast<v4i *>(lds) + (t & 1) * T::STAGE;
 #pragma unroll
         for (int i = 0; i < T::LA; ++i)
             st[(i * T::NW + wave) * 64 + lane] = aset[i];
+#pragma unroll
+        for (int i = 0; i < T::LW8; ++i)
+            st[(T::AIMG + i * T::NW + wave) * 64 + lane] = wset[i];
+    };
+    // LDS path: this wave's weight operands of stage t (its k-group's
+    // k-block): for 32-channel group j the images 2*(wn*FN+j) + (l>>4 & 1),
+    // slot 16*(2h + l/32) + l%16, as the direct path loads them.
+    auto bread = [&](int t, v4i (&b)[T::FN][2]) __attribute__((always_inline)) {
+        const v4i *st = reinterpret_cast<const v4i *>(lds) + (t & 1) * T::STAGE +
+                        (T::AIMG + wk * (T::BN / 16)) * 64;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j)
+                b[j][h] = st[(2 * (wn * T::FN + j) + ((lane >> 4) & 1)) * 64 + 16 * (2 * h + (lane >> 5)) +
+                             (lane & 15)];
     };
     // This wave's token operands of stage t (its k-group's k-block) from LDS.
     auto read = [&](int t, v4i (&x)[T::FM][2]) __attribute__((always_inline)) {
@@ -364,7 +408,9 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
     // Memory instructions placed after each MFMA of the interleave: one for
     // int8; the e4m3 twin has half as many (twice as long) MFMAs, so its
     // memory instructions are spread over them.
-    constexpr int MEM_OPS = 2 * T::FM + T::LA + T::LPW;
+    constexpr int DS_READS = 2 * T::FM + (T::WLDS ? 2 * T::FN : 0);
+    constexpr int DS_WRITES = T::LA + T::LW8;
+    constexpr int MEM_OPS = DS_READS + DS_WRITES + T::LPW;
     constexpr int PER = FP8 ? (MEM_OPS + NMMA - PRE - 1) / (NMMA - PRE) : 1;
 
     // Step s. On entry stage s+1 is being written to LDS by every wave, this
@@ -384,29 +430,41 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
             wait_vm_lgkm0<T::VM>();
         else
             wait_lgkm0();
+        auto &wcur = [&]() -> auto & {
+            if constexpr (T::WLDS)
+                return bf[u & 1];
+            else
+                return bq[u % T::NB];
+        }();
         if (run)
-            mma(std::integral_constant<int, 0>{}, std::integral_constant<int, PRE>{}, xf[u & 1],
-                bq[u % T::NB]);
+            mma(std::integral_constant<int, 0>{}, std::integral_constant<int, PRE>{}, xf[u & 1], wcur);
         __builtin_amdgcn_s_barrier();
-        if (FULL || s + 1 < S)
+        if (FULL || s + 1 < S) {
             read(s + 1, xf[(u + 1) & 1]);
+            if constexpr (T::WLDS)
+                bread(s + 1, bf[(u + 1) & 1]);
+        }
         if (FULL || s + 2 < S)
-            store(s + 2, ast[(u + 2) % T::NA]);
-        if (FULL || s + 2 + T::LT < S)
+            store(s + 2, ast[(u + 2) % T::NA], bst[(u + 2) % T::NA]);
+        if (FULL || s + 2 + T::LT < S) {
             load_a(s + 2 + T::LT, ast[(u + 2) % T::NA]);
-        if (FULL || s + T::LW < S)
-            load_b(s + T::LW, bq[(u + T::LW) % T::NB]);
+            if constexpr (T::WLDS)
+                load_w(s + 2 + T::LT, bst[(u + 2) % T::NA]);
+        }
+        if constexpr (!T::WLDS) {
+            if (FULL || s + T::LW < S)
+                load_b(s + T::LW, bq[(u + T::LW) % T::NB]);
+        }
         if (run)
-            mma(std::integral_constant<int, PRE>{}, std::integral_constant<int, NMMA>{}, xf[u & 1],
-                bq[u % T::NB]);
+            mma(std::integral_constant<int, PRE>{}, std::integral_constant<int, NMMA>{}, xf[u & 1], wcur);
         if (FULL) {
             // One memory instruction after each MFMA: operand reads first,
             // then the LDS writes, then the global loads.
-            static_for<(2 * T::FM + PER - 1) / PER>([&](auto) __attribute__((always_inline)) {
+            static_for<(DS_READS + PER - 1) / PER>([&](auto) __attribute__((always_inline)) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x100, PER, 0); // DS read
             });
-            static_for<(T::LA + PER - 1) / PER>([&](auto) __attribute__((always_inline)) {
+            static_for<(DS_WRITES + PER - 1) / PER>([&](auto) __attribute__((always_inline)) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x200, PER, 0); // DS write
             });
@@ -474,21 +532,32 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
     // loop entry matches the one at the back-edge and the waits the
     // compiler derives inside the loop stay as loose as the steady state.
     load_a(0, ast[0]);
+    if constexpr (T::WLDS)
+        load_w(0, bst[0]);
     load_a(1, ast[1 % T::NA]);
-    static_for<T::LW - T::LT>([&](auto U) __attribute__((always_inline)) {
-        constexpr int t = decltype(U)::value;
-        load_b(t, bq[t % T::NB]);
-    });
-    store(0, ast[0]);
-    store(1, ast[1 % T::NA]);
+    if constexpr (T::WLDS) {
+        load_w(1, bst[1 % T::NA]);
+    } else {
+        static_for<T::LW - T::LT>([&](auto U) __attribute__((always_inline)) {
+            constexpr int t = decltype(U)::value;
+            load_b(t, bq[t % T::NB]);
+        });
+    }
+    store(0, ast[0], bst[0]);
+    store(1, ast[1 % T::NA], bst[1 % T::NA]);
     static_for<T::LT>([&](auto U) __attribute__((always_inline)) {
         constexpr int v = decltype(U)::value - T::LT;  // virtual step -LT .. -1
         load_a(v + 2 + T::LT, ast[(v + 2 + T::LT) % T::NA]);
-        load_b(v + T::LW, bq[(v + T::LW) % T::NB]);
+        if constexpr (T::WLDS)
+            load_w(v + 2 + T::LT, bst[(v + 2 + T::LT) % T::NA]);
+        else
+            load_b(v + T::LW, bq[(v + T::LW) % T::NB]);
     });
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
     read(0, xf[0]);
+    if constexpr (T::WLDS)
+        bread(0, bf[0]);
 
     // Steady state: GROUP unconditional steps while every stage they fetch
     // exists.
@@ -698,14 +767,16 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
 // The main kernel's tile configurations in tile-number order (the int8
 // kernel and its e4m3 twin use the same list): BM x BN output tile / WM row
 // groups x WN column groups x WK k-groups of waves / token and weight fetch
-// leads in stages.
+// leads in stages ("l2lds": weights through LDS in the token pipeline, two
+// stages ahead; measured on MI355X 6-9 % faster than fetching them straight
+// into registers, where the two row groups each load every fragment).
 using MainTiles = std::tuple<Tile<64, 64, 1, 2, 2, 2, 3>, Tile<64, 128, 1, 2, 2, 2, 3>,
                              Tile<128, 64, 1, 2, 2, 2, 3>, Tile<128, 128, 1, 2, 2, 2, 3>,
-                             Tile<128, 192, 1, 2, 2, 2, 3>, Tile<256, 128, 2, 2, 1, 2, 3>,
-                             Tile<256, 192, 2, 2, 1, 2, 3>>;
+                             Tile<128, 192, 1, 2, 2, 2, 3>, Tile<256, 128, 2, 2, 1, 2, 3, true>,
+                             Tile<256, 192, 2, 2, 1, 2, 3, true>>;
 constexpr const char *kMainTileNames[] = {
-    "64x64/m1n2k2/l23",   "64x128/m1n2k2/l23",  "128x64/m1n2k2/l23",  "128x128/m1n2k2/l23",
-    "128x192/m1n2k2/l23", "256x128/m2n2k1/l23", "256x192/m2n2k1/l23"};
+    "64x64/m1n2k2/l23",   "64x128/m1n2k2/l23",    "128x64/m1n2k2/l23",    "128x128/m1n2k2/l23",
+    "128x192/m1n2k2/l23", "256x128/m2n2k1/l2lds", "256x192/m2n2k1/l2lds"};
 constexpr int kNumMainTiles = (int)std::tuple_size<MainTiles>::value;
 static_assert(sizeof(kMainTileNames) / sizeof(kMainTileNames[0]) == kNumMainTiles, "tile names");
 
