@@ -667,6 +667,8 @@ def main(argv=None) -> int:
 
     if not args.no_decode:
         rec["decode"] = decode_record(torch, ops)
+        rec["decode_ffn_down"] = decode_record(torch, ops, M=8, N=3072, K=12288,
+                                               label="FFN down-projection")
     if not args.no_quant_large:
         rec["quant_large"] = quant_bandwidth(torch, L, wl, stream, args.steps)
         rec["hbm_copy_reference"] = copy_reference(torch, args.steps)
@@ -684,14 +686,16 @@ def main(argv=None) -> int:
     return 0
 
 
-def decode_record(torch, ops, M: int = 1, N: int = 12288, K: int = 4096, launches: int = 0) -> dict:
-    """The fused-QKV layer at one token (decode): int8_quant_scaled_mm through
-    the small-M kernel, rotating over weight copies larger than the 256 MB
-    last-level cache (each call streams its weight from HBM, as a model's
-    layers would), replayed from a HIP graph so that host launch costs stay
-    out of the timing. Every replay's output is checked against the eager
-    result. Weights and activations are seeded random data of the layer's
-    shape."""
+def decode_record(torch, ops, M: int = 1, N: int = 12288, K: int = 4096, launches: int = 0,
+                  label: str = "fused-QKV layer") -> dict:
+    """A layer at a few tokens (decode): int8_quant_scaled_mm through the
+    small-M kernel, with the layer's workspace (K split over workgroups when
+    the weight has too few column blocks to keep every CU streaming),
+    rotating over weight copies larger than the 256 MB last-level cache
+    (each call streams its weight from HBM, as a model's layers would),
+    replayed from a HIP graph so that host launch costs stay out of the
+    timing. Every replay's output is checked against the eager result.
+    Weights and activations are seeded random data of the layer's shape."""
     g = torch.Generator(device="cpu").manual_seed(20251)
     w = torch.randint(-127, 128, (N, K), dtype=torch.int8, generator=g).cuda()
     x = (torch.randn((M, K), generator=g) * 2.0).to(torch.bfloat16).cuda()
@@ -702,11 +706,12 @@ def decode_record(torch, ops, M: int = 1, N: int = 12288, K: int = 4096, launche
     xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
     xs = torch.empty((M,), dtype=torch.float32, device="cuda")
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    work = ops.new_workspace(N, K, max_rows=M)
     ref = ops.quant_scaled_mm(x, packed, ws, N)[0]
     reps = 2 * copies
     if launches:                   # profiler runs: plain eager launches, nothing timed
         for i in range(launches):
-            ops.quant_scaled_mm(x, packs[i % copies], ws, N, out=out, xq=xq, xs=xs)
+            ops.quant_scaled_mm(x, packs[i % copies], ws, N, out=out, xq=xq, xs=xs, workspace=work)
         torch.cuda.synchronize()
         return {}
 
@@ -737,19 +742,22 @@ def decode_record(torch, ops, M: int = 1, N: int = 12288, K: int = 4096, launche
             ts.append(e0.elapsed_time(e1) * 1e3 / reps)
         return float(np.median(ts))
 
-    step = replay_us(capture(lambda p: ops.quant_scaled_mm(x, p, ws, N, out=out, xq=xq, xs=xs)))
+    step = replay_us(capture(lambda p: ops.quant_scaled_mm(x, p, ws, N, out=out, xq=xq, xs=xs,
+                                                           workspace=work)))
     ops.quant_per_token(x, xq, xs)
-    mm = replay_us(capture(lambda p: ops.scaled_mm(xq, xs, p, ws, N, out=out)))
+    mm = replay_us(capture(lambda p: ops.scaled_mm(xq, xs, p, ws, N, out=out, workspace=work)))
     wbytes = packed.numel()
-    rec = {"workload": f"fused-QKV layer at {M} token(s): M={M} K={K} N={N}, bf16 out, no bias",
+    rec = {"workload": f"{label} at {M} token(s): M={M} K={K} N={N}, bf16 out, no bias",
            "tile": ops.tile_name(ops.tile_auto(M, N, K)),
+           "workspace_bytes": ops.workspace_bytes(M, N, K),
            "weight_copies": copies, "timing": "HIP graph replay, median per call",
            "step_us": round(step, 3), "scaled_mm_us": round(mm, 3),
            "weight_bytes": wbytes,
            "step_weight_gbps": round(wbytes / (step * 1e-6) / 1e9, 1),
            "scaled_mm_weight_gbps": round(wbytes / (mm * 1e-6) / 1e9, 1),
            "scaled_mm_frac_hbm_peak": round(wbytes / (mm * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
-           "step_traffic": traffic_record("int8_quant_scaled_mm", "fused_qkv_m1")}
+           "step_traffic": traffic_record("int8_quant_scaled_mm",
+                                          ("fused_qkv" if N == 12288 else "ffn_down") + f"_m{M}")}
     del packs, packed, w
     torch.cuda.empty_cache()
     return rec

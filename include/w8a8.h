@@ -259,6 +259,59 @@ w8a8_status_t int8_quant_scaled_mm(const uint16_t *x, int64_t ldx, int8_t *xq, i
                                    void *out, int64_t ldo, void *stream);
 
 /*
+ * int8_scaled_mm_workspace_bytes - bytes of workspace that int8_scaled_mm_ws
+ * and int8_quant_scaled_mm_ws use for an M x N x K product (automatic tile),
+ * or 0 when that shape runs without one.
+ *
+ * A workspace serves the small-M (decode-shaped) kernel when the weight has
+ * too few 16-channel column blocks to keep every CU streaming it (page
+ * "INT8 Quant for Dual-Max Recipe", controlled-run takeaways: decode is
+ * bound by moving the weight): K is then split over 2 to 8 workgroups per
+ * tile. Each takes a ticket from a per-tile arrival word; all but the last
+ * leave their int32 partial sums in the workspace and count themselves in a
+ * second per-tile word; the last waits for that count, adds the partial
+ * sums up (exact in int32, so the output is bit-identical to the unsplit
+ * one), applies the epilogue and sets both words back to 0. Layout: the
+ * per-tile words (8 bytes per tile, rounded up to 256 bytes), then 1 KB of
+ * partial sums per 16 x 16 fragment pair of each split. Arguments out of
+ * range give 0.
+ */
+size_t int8_scaled_mm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * int8_scaled_mm_ws - int8_scaled_mm (automatic tile) with a workspace
+ * (device memory, 256-byte aligned, workspace_bytes long) that the split of
+ * K described at int8_scaled_mm_workspace_bytes uses when the shape calls
+ * for one and workspace_bytes is at least that many bytes; otherwise the
+ * call runs as int8_scaled_mm. Results are bit-identical either way.
+ *
+ * The workspace's per-tile words must be zero before its first use (zero it
+ * once when allocating it); every call leaves them zero. The caller owns it
+ * and keeps it alive until the stream has run the call. Calls that overlap
+ * on one workspace (two streams, or graph replays that run concurrently)
+ * race: give each concurrent caller its own. workspace may be NULL (no
+ * split). Errors: those of int8_scaled_mm, plus W8A8_ERR_ALIGN for a
+ * workspace that is used but not 256-byte aligned.
+ */
+w8a8_status_t int8_scaled_mm_ws(const int8_t *xq, int64_t ldq, const float *x_scale,
+                                const void *w_packed, const float *w_scale, const uint16_t *bias,
+                                int64_t M, int64_t N, int64_t K, int mode, void *out, int64_t ldo,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * int8_quant_scaled_mm_ws - int8_quant_scaled_mm (bf16 activations,
+ * automatic tile) with a workspace for the split of K, on the terms of
+ * int8_scaled_mm_ws. The split applies to the small-M kernel (its fused
+ * quant included; the workgroups of the first column block and first split
+ * write xq and x_scale).
+ */
+w8a8_status_t int8_quant_scaled_mm_ws(const uint16_t *x, int64_t ldx, int8_t *xq, int64_t ldq,
+                                      float *x_scale, const void *w_packed, const float *w_scale,
+                                      const uint16_t *bias, int64_t M, int64_t N, int64_t K,
+                                      int mode, void *out, int64_t ldo, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/*
  * int8_quant_scaled_mm_f16 - int8_quant_scaled_mm for fp16 activations x
  * (fp16 bits, [M, ldx]): int8_quant_per_token_f16 of x, then int8_scaled_mm
  * of the result, bit-identical to those two calls. With mode W8A8_OUT_F16

@@ -277,18 +277,60 @@ w8a8_status_t mm_args(const int8_t *xq, int64_t ldq, const float *x_scale, const
 
 }  // namespace
 
-W8A8_API w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const float *x_scale,
-                                           const void *w_packed, const float *w_scale,
-                                           const uint16_t *bias, int64_t M, int64_t N, int64_t K,
-                                           int mode, void *out, int64_t ldo, void *stream,
-                                           int tile)
+namespace {
+
+// The split of K that tile t would use for an M x N x K product, and the
+// workspace bytes it needs (0: no split for this shape and tile).
+size_t split_need(int t, int64_t M, int64_t N, int64_t K, w8a8::SkinnySplit *split = nullptr)
 {
-    const char *what = "int8_scaled_mm";
+    if (M < 1 || N < 1 || K < 1 || t < 0)
+        return 0;
+    const w8a8::TileEntry &e = w8a8::mm_tile_entry(t);
+    if (!e.skinny)
+        return 0;
+    const int64_t tiles = w8a8::ceil_div(M, e.bm) * w8a8::ceil_div(N, e.bn);
+    const w8a8::SkinnySplit sp = w8a8::skinny_split(tiles, e.bm / 16, e.bn / 16, e.threads / 64,
+                                                    (int)w8a8::ceil_div(K, w8a8::kFragK));
+    if (split)
+        *split = sp;
+    if (!w8a8::mm_grid_fits(tiles * sp.ksplit, e.threads))
+        return 0;
+    return sp.bytes();
+}
+
+// Hands the caller's workspace to the launch when tile t splits K for this
+// shape and the workspace is large enough; otherwise the launch runs
+// unsplit (same results).
+w8a8_status_t take_workspace(w8a8::MmArgs &a, int t, void *workspace, size_t workspace_bytes,
+                             const char *what)
+{
+    w8a8::SkinnySplit sp{};
+    const size_t need = split_need(t, a.M, a.N, a.K, &sp);
+    if (need == 0 || workspace == nullptr || workspace_bytes < need)
+        return W8A8_OK;
+    if (!aligned(workspace, 256))
+        return fail(W8A8_ERR_ALIGN, "%s: workspace must be 256-byte aligned", what);
+    a.ksplit = sp.ksplit;
+    a.kbs = sp.kbs;
+    a.split_count = reinterpret_cast<unsigned *>(workspace);
+    a.split_part = reinterpret_cast<int *>(reinterpret_cast<char *>(workspace) + sp.count_bytes);
+    return W8A8_OK;
+}
+
+w8a8_status_t scaled_mm_common(const int8_t *xq, int64_t ldq, const float *x_scale,
+                               const void *w_packed, const float *w_scale, const uint16_t *bias,
+                               int64_t M, int64_t N, int64_t K, int mode, void *out, int64_t ldo,
+                               void *workspace, size_t workspace_bytes, void *stream, int tile,
+                               const char *what)
+{
     w8a8::MmArgs a;
     int t;
     w8a8_status_t st = mm_args(xq, ldq, x_scale, w_packed, w_scale, bias, M, N, K, mode, out, ldo,
                                tile, false, what, a, t);
     if (st != W8A8_OK || M == 0)
+        return st;
+    st = take_workspace(a, t, workspace, workspace_bytes, what);
+    if (st != W8A8_OK)
         return st;
     st = check_device();
     if (st != W8A8_OK)
@@ -297,13 +339,43 @@ W8A8_API w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const 
                     what);
 }
 
+}  // namespace
+
+W8A8_API w8a8_status_t int8_scaled_mm_tile(const int8_t *xq, int64_t ldq, const float *x_scale,
+                                           const void *w_packed, const float *w_scale,
+                                           const uint16_t *bias, int64_t M, int64_t N, int64_t K,
+                                           int mode, void *out, int64_t ldo, void *stream,
+                                           int tile)
+{
+    return scaled_mm_common(xq, ldq, x_scale, w_packed, w_scale, bias, M, N, K, mode, out, ldo,
+                            nullptr, 0, stream, tile, "int8_scaled_mm");
+}
+
+W8A8_API size_t int8_scaled_mm_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 1 || M > kMaxRows || N < 1 || N > kMaxRows || K < 16 || K > W8A8_MAX_K || K % 16 != 0)
+        return 0;
+    return split_need(w8a8::mm_tile_auto(M, N, K), M, N, K);
+}
+
+W8A8_API w8a8_status_t int8_scaled_mm_ws(const int8_t *xq, int64_t ldq, const float *x_scale,
+                                         const void *w_packed, const float *w_scale,
+                                         const uint16_t *bias, int64_t M, int64_t N, int64_t K,
+                                         int mode, void *out, int64_t ldo, void *workspace,
+                                         size_t workspace_bytes, void *stream)
+{
+    return scaled_mm_common(xq, ldq, x_scale, w_packed, w_scale, bias, M, N, K, mode, out, ldo,
+                            workspace, workspace_bytes, stream, -1, "int8_scaled_mm_ws");
+}
+
 namespace {
 
 // The fused entry points for bf16 and fp16 activations (x_kind).
 w8a8_status_t quant_mm_common(const uint16_t *x, int x_kind, int64_t ldx, int8_t *xq, int64_t ldq,
                               float *x_scale, const void *w_packed, const float *w_scale,
                               const uint16_t *bias, int64_t M, int64_t N, int64_t K, int mode,
-                              void *out, int64_t ldo, void *stream, int tile, const char *what)
+                              void *out, int64_t ldo, void *stream, int tile, const char *what,
+                              void *workspace = nullptr, size_t workspace_bytes = 0)
 {
     w8a8::MmArgs a;
     int t;
@@ -319,6 +391,9 @@ w8a8_status_t quant_mm_common(const uint16_t *x, int x_kind, int64_t ldx, int8_t
         return fail(W8A8_ERR_NULL, "%s: NULL tensor pointer", what);
     if (!aligned(x, 16) || ldx % 8 != 0)
         return fail(W8A8_ERR_ALIGN, "%s: x must be 16-byte aligned with ldx a multiple of 8", what);
+    st = take_workspace(a, t, workspace, workspace_bytes, what);
+    if (st != W8A8_OK)
+        return st;
     st = check_device();
     if (st != W8A8_OK)
         return st;
@@ -385,6 +460,18 @@ W8A8_API w8a8_status_t int8_quant_scaled_mm(const uint16_t *x, int64_t ldx, int8
 {
     return int8_quant_scaled_mm_tile(x, ldx, xq, ldq, x_scale, w_packed, w_scale, bias, M, N, K,
                                      mode, out, ldo, stream, -1);
+}
+
+W8A8_API w8a8_status_t int8_quant_scaled_mm_ws(const uint16_t *x, int64_t ldx, int8_t *xq,
+                                               int64_t ldq, float *x_scale, const void *w_packed,
+                                               const float *w_scale, const uint16_t *bias,
+                                               int64_t M, int64_t N, int64_t K, int mode,
+                                               void *out, int64_t ldo, void *workspace,
+                                               size_t workspace_bytes, void *stream)
+{
+    return quant_mm_common(x, w8a8::kElemBF16, ldx, xq, ldq, x_scale, w_packed, w_scale, bias, M,
+                           N, K, mode, out, ldo, stream, -1, "int8_quant_scaled_mm_ws", workspace,
+                           workspace_bytes);
 }
 
 W8A8_API w8a8_status_t int8_scaled_mm(const int8_t *xq, int64_t ldq, const float *x_scale,

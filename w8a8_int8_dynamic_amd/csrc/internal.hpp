@@ -69,7 +69,28 @@ struct MmArgs {
     int rows_per_wg;
     unsigned epoch;       // this launch's number on its device, never 0
     unsigned wait_limit;  // bound on a workgroup's polls for its producers' flags
+    // Split of K over workgroups (small-M kernel only; ksplit <= 1: none).
+    // Each tile's ksplit workgroups take kbs k-blocks each; two words per
+    // tile in split_count (arrivals, partial sums written) and the partial
+    // sums in split_part let the last to arrive add them up and apply the
+    // epilogue; it sets both words back to 0.
+    int ksplit;
+    int kbs;
+    unsigned *split_count;
+    int *split_part;
 };
+
+// Split of K for the small-M kernel: how many workgroups share a tile's K
+// (1: no split) and the workspace the split needs (counters, then the
+// partial sums), for `tiles` tiles of fm x fn 16 x 16 fragments and kblocks
+// k-blocks spread over wk waves per workgroup.
+struct SkinnySplit {
+    int ksplit, kbs;
+    size_t count_bytes, part_bytes;
+    size_t bytes() const { return ksplit > 1 ? count_bytes + part_bytes : 0; }
+};
+SkinnySplit skinny_split(int64_t tiles, int fm, int fn, int wk, int kblocks);
+
 
 // Output kinds, the ABI's W8A8_OUT_* values: they index TileEntry's kernels.
 constexpr int kOutBF16 = 0, kOutI32 = 1, kOutF16 = 2, kOutKinds = 3;
@@ -107,6 +128,7 @@ __device__ __forceinline__ int xcd_remap(int pid, int tiles)
 }
 
 int mm_tile_count();
+const TileEntry &mm_tile_entry(int tile);     // int8 tiles: main, then small-M
 const char *mm_tile_name(int tile);
 int mm_tile_auto(int64_t M, int64_t N, int64_t K);
 // Whether the grid of tile `tile` over an M x N output fits one launch

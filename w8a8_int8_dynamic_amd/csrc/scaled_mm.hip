@@ -33,6 +33,8 @@ const TileEntry &tile_entry(int tile)
 
 }  // namespace
 
+const TileEntry &mm_tile_entry(int tile) { return tile_entry(tile); }
+
 int mm_tile_count() { return kNumTiles + skinny_tile_count(); }
 
 bool mm_launch_fits(int tile, int64_t M, int64_t N)
@@ -95,7 +97,8 @@ int mm_tile_auto(int64_t M, int64_t N, int64_t K)
 hipError_t launch_scaled_mm(const MmArgs &a, int mode, int tile, hipStream_t stream)
 {
     const TileEntry &e = tile_entry(tile);
-    const int64_t tiles = ceil_div(a.M, e.bm) * ceil_div(a.N, e.bn);
+    const int64_t tiles = ceil_div(a.M, e.bm) * ceil_div(a.N, e.bn) *
+                          (e.skinny && a.ksplit > 1 ? a.ksplit : 1);
     const int threads = e.threads;
     hipLaunchKernelGGL(e.plain[mode], dim3((unsigned)tiles), dim3(threads), 0, stream, a);
     return hipGetLastError();

@@ -158,10 +158,16 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
     const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int tiles_m = (a.M + S::BM - 1) / S::BM;
     const int tiles_n = (a.nblocks + S::FN - 1) / S::FN;
+    // Split of K (int8 only): the nsplit workgroups of a tile are neighbours
+    // in the logical order, each with its own run of kbs k-blocks.
+    const int nsplit = !FP8 && a.ksplit > 1 ? a.ksplit : 1;
     // The row tiles of one weight column run on one XCD, next to each other.
-    const int t = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+    const int tl = xcd_remap(blockIdx.x, tiles_m * tiles_n * nsplit);
+    const int t = tl / nsplit, ks = tl - t * nsplit;
     const int m0 = (t % tiles_m) * S::BM, nb0 = (t / tiles_m) * S::FN;
     const int KB = a.kblocks;
+    const int kbeg = nsplit > 1 ? min(ks * a.kbs, KB) : 0;
+    const int kend = nsplit > 1 ? min(kbeg + a.kbs, KB) : KB;
     const int klast = a.K - 16;
 
     const v4i *wsrc[S::FN];
@@ -250,11 +256,18 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
     // first MFMA waits on any of them. Each workgroup starts its walk at its
     // own offset (rot), which spreads the workgroups of an XCD over the
     // token bytes.
-    const int mine = wk < KB ? (KB - 1 - wk) / S::WK + 1 : 0;
+    // The split's ticket is taken as the workgroup starts (by wave 0, which
+    // finishes the tile), so its round trip overlaps the K loop.
+    unsigned ticket0 = 0;
+    if (nsplit > 1 && wk == 0 && lane == 0)
+        ticket0 = __hip_atomic_fetch_add(a.split_count + 2 * t, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    const int span = kend - kbeg;
+    const int mine = wk < span ? (span - 1 - wk) / S::WK + 1 : 0;
     const int rot = mine > 0 ? t % mine : 0;
     auto kb_of = [&](int i) __attribute__((always_inline)) {
         i += rot;
-        return wk + (i >= mine ? i - mine : i) * S::WK;
+        return kbeg + wk + (i >= mine ? i - mine : i) * S::WK;
     };
     int g = 0;
     if (FUSED) {
@@ -266,7 +279,8 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
 #pragma unroll
         for (int u = 0; u < S::U; ++u)
             wload(min(kb_of(u), KB - 1), w[u]);
-        quantize_tile<S::THREADS, IN, FP8>(a, m0, rows, pitch, nb0 == 0, tok, rowmax, rowscale);
+        quantize_tile<S::THREADS, IN, FP8>(a, m0, rows, pitch, nb0 == 0 && ks == 0, tok, rowmax,
+                                           rowscale);
         if (pre) {
             v4i x[S::U][S::FM];
 #pragma unroll
@@ -317,6 +331,66 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
 #pragma unroll
             for (int j = 0; j < S::FN; ++j)
                 acc[f][j] += __builtin_bit_cast(Acc, part[w][f * S::FN + j][lane]);
+
+    if (nsplit > 1) {
+        // The tile's nsplit workgroups meet through the workspace: each
+        // took a ticket from the tile's arrival word as it started (in start
+        // order, so the last ticket may go to a workgroup that finishes
+        // early; it then waits for the others); all but the last
+        // write their int32 partial sums (write-through stores, coherent
+        // across the XCDs once complete) and then count themselves in the
+        // tile's done word. The last waits until done shows the others,
+        // reads their partial sums with coherent loads, adds them (exact in
+        // int32, whatever the order), finishes the tile and sets both words
+        // back to 0. It only ever waits for workgroups that hold a ticket,
+        // so are running and never wait themselves: the wait always ends.
+        unsigned *words = a.split_count + 2 * t;     // [0] arrivals, [1] done
+        const unsigned ticket = (unsigned)__builtin_amdgcn_readfirstlane((int)ticket0);
+        uint64_t *part_all = reinterpret_cast<uint64_t *>(a.split_part) +
+                             (int64_t)t * nsplit * (S::FM * S::FN * 64 * 2);
+        if (ticket != (unsigned)(nsplit - 1)) {
+            uint64_t *mine_part = part_all + (int64_t)ks * (S::FM * S::FN * 64 * 2);
+#pragma unroll
+            for (int f = 0; f < S::FM; ++f)
+#pragma unroll
+                for (int j = 0; j < S::FN; ++j) {
+                    const v4i v = __builtin_bit_cast(v4i, acc[f][j]);
+                    uint64_t *d = mine_part + ((f * S::FN + j) * 64 + lane) * 2;
+                    __hip_atomic_store(d, (uint64_t)(unsigned)v[1] << 32 | (unsigned)v[0],
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(d + 1, (uint64_t)(unsigned)v[3] << 32 | (unsigned)v[2],
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            __builtin_amdgcn_s_waitcnt(0);             // every store above has completed
+            if (lane == 0)
+                __hip_atomic_fetch_add(words + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        while (__hip_atomic_load(words + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
+               (unsigned)(nsplit - 1))
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll 1
+        for (int o = 0; o < nsplit; ++o) {
+            if (o == ks)
+                continue;
+            const uint64_t *src = part_all + (int64_t)o * (S::FM * S::FN * 64 * 2);
+#pragma unroll
+            for (int f = 0; f < S::FM; ++f)
+#pragma unroll
+                for (int j = 0; j < S::FN; ++j) {
+                    const uint64_t *q = src + ((f * S::FN + j) * 64 + lane) * 2;
+                    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const v4i v = {(int)(unsigned)lo, (int)(unsigned)(lo >> 32), (int)(unsigned)hi,
+                                   (int)(unsigned)(hi >> 32)};
+                    acc[f][j] += __builtin_bit_cast(Acc, v);
+                }
+        }
+        if (lane == 0) {
+            __hip_atomic_store(words, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(words + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 
     const bool has_bias = !OUT_I32 && a.bias != nullptr;
 #pragma unroll
@@ -385,6 +459,7 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
 template <class S>
 constexpr TileEntry skinny(const char *name)
 {
+    static_assert(S::U == 4, "skinny_split counts load groups of 4 k-blocks");
     return TileEntry{name, S::BM, S::BN, S::THREADS, true,
                      {skinny_mm_kernel<S, kOutBF16, false>, skinny_mm_kernel<S, kOutI32, false>,
                       skinny_mm_kernel<S, kOutF16, false>},
@@ -437,10 +512,38 @@ hipError_t launch_skinny_quant_mm(const MmArgs &a, const TileEntry &e, int mode,
     if (rows > kQuantRows || rows * cpr > kQuantSlots)
         return hipErrorNotSupported;
     const size_t lds = (size_t)(rows * (a.K + 16));
-    const int64_t tiles = ceil_div(a.M, e.bm) * ceil_div(a.N, e.bn);
+    const int64_t tiles = ceil_div(a.M, e.bm) * ceil_div(a.N, e.bn) * (a.ksplit > 1 ? a.ksplit : 1);
     hipLaunchKernelGGL(e.fused[mode], dim3((unsigned)tiles), dim3(e.threads),
                        lds, stream, a);
     return hipGetLastError();
+}
+
+SkinnySplit skinny_split(int64_t tiles, int fm, int fn, int wk, int kblocks)
+{
+    // A wave walks its k-blocks in load groups of kGroup, one memory round
+    // trip each, so an unsplit tile takes about kblocks / (wk * kGroup)
+    // round trips; meeting the other workgroups of a split through memory
+    // costs about three (measured on MI355X: 3-5 us). Split only where the
+    // chain is long (at least 12 groups: K of 24576 and more on eight
+    // waves), into as many as 8 ways that leave at least 4 groups each and
+    // at most about two workgroups per CU. Measured: K 131056, N 16: 48.4 ->
+    // 12.1 us; K 65536, N 512: 27.1 -> 13.3 us; K 32768, N 1024, 4 rows:
+    // 16.8 -> 14.6 us; K 12288, N 3072 (6 groups): 9.3 us unsplit against
+    // 15.9 split, so no split there.
+    constexpr int kGroup = 4;               // every small-M configuration's U
+    const int64_t chain = ceil_div(kblocks, (int64_t)wk * kGroup);
+    SkinnySplit r{1, kblocks, 0, 0};
+    if (chain >= 12) {
+        for (int s = 2; s <= 8; s *= 2) {
+            if (tiles * (s / 2) >= 512 || chain / s < 4)
+                break;
+            r.ksplit = s;
+        }
+    }
+    r.kbs = (int)ceil_div(kblocks, r.ksplit);
+    r.count_bytes = (size_t)round_up(tiles * 8, 256);
+    r.part_bytes = (size_t)tiles * r.ksplit * fm * fn * 1024;
+    return r;
 }
 
 }  // namespace w8a8

@@ -43,6 +43,14 @@ class W8A8Linear(torch.nn.Module):
         # The bias in each output type, rounded once from what was given.
         self.register_buffer("bias", None if bias is None else bias.to(torch.bfloat16).contiguous())
         self.register_buffer("bias_f16", None if bias is None else bias.to(torch.float16).contiguous())
+        # The layer's own workspace for decode-shaped calls (a handful of
+        # tokens against a weight with few column blocks), allocated once
+        # here so that forward never allocates it.
+        self.register_buffer(
+            "workspace",
+            ops.new_workspace(out_features, in_features, device=w_packed.device)
+            if scheme == "int8" and w_packed.is_cuda else None,
+            persistent=False)
 
     @classmethod
     def from_quantized(cls, wq: torch.Tensor, w_scale: torch.Tensor,
@@ -83,8 +91,9 @@ class W8A8Linear(torch.nn.Module):
             out, _, _ = ops.fp8_quant_scaled_mm(x2, self.w_packed, self.w_scale,
                                                 self.out_features, bias)
         else:
+            wsp = self.workspace if x2.dtype == torch.bfloat16 else None
             out, _, _ = ops.quant_scaled_mm(x2, self.w_packed, self.w_scale, self.out_features,
-                                            bias)
+                                            bias, workspace=wsp)
         return out.reshape(*lead, self.out_features)
 
     def extra_repr(self) -> str:

@@ -17,6 +17,7 @@ from ._lib import W8A8_OUT_BF16, W8A8_OUT_F16, W8A8_OUT_I32, call
 
 __all__ = ["quant_per_token", "quant_per_channel", "prepack_weight", "quant_prepack_weight", "unpack_weight",
            "prepack_weight_bytes", "scaled_mm", "quant_scaled_mm", "tile_count", "tile_name",
+           "workspace_bytes", "new_workspace",
            "tile_auto", "device_supported", "fp8_quant_per_token", "fp8_quant_per_channel",
            "fp8_quant_prepack_weight", "fp8_scaled_mm", "fp8_quant_scaled_mm", "fp8_tile_count"]
 
@@ -177,12 +178,39 @@ def unpack_weight(packed: torch.Tensor, N: int, K: int) -> torch.Tensor:
     return wq
 
 
+def workspace_bytes(M: int, N: int, K: int) -> int:
+    """Bytes of workspace the split of K uses for an M x N x K product (0: none)."""
+    return int(_lib.lib().int8_scaled_mm_workspace_bytes(M, N, K))
+
+
+def new_workspace(N: int, K: int, max_rows: int = 32, device=None) -> Optional[torch.Tensor]:
+    """A zeroed workspace large enough for every M up to max_rows against an
+    N x K weight (None when no such shape splits K). Give each stream (or
+    each concurrently replayed graph) its own."""
+    need = max(workspace_bytes(m, N, K) for m in range(1, max_rows + 1))
+    if need == 0:
+        return None
+    if device is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    return torch.zeros((need,), dtype=torch.uint8, device=device)
+
+
+def _workspace(workspace: Optional[torch.Tensor]):
+    if workspace is None:
+        return None, 0
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def scaled_mm(xq: torch.Tensor, xs: Optional[torch.Tensor], w_packed: torch.Tensor,
               ws: Optional[torch.Tensor], N: int, bias: Optional[torch.Tensor] = None,
               out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
-              tile: int = -1) -> torch.Tensor:
+              tile: int = -1, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out[m, n] = acc * xs[m] * ws[n] (+ bias[n]) rounded to out_dtype (bf16 or fp16;
-    the bias in the same type), or the int32 accumulators when out_dtype=int32."""
+    the bias in the same type), or the int32 accumulators when out_dtype=int32.
+    With a workspace (from new_workspace; automatic tile only) decode-shaped
+    products may split K over workgroups; results are bit-identical."""
     _matrix(xq, "xq", torch.int8)
     M, K = xq.shape
     mode = _out_mode(out_dtype)
@@ -201,6 +229,15 @@ def scaled_mm(xq: torch.Tensor, xs: Optional[torch.Tensor], w_packed: torch.Tens
         return None if t is None or mode == W8A8_OUT_I32 else t.data_ptr()
 
     _same_device(xq, w_packed, out, *((xs, ws, bias) if mode != W8A8_OUT_I32 else ()))
+    if workspace is not None:
+        if tile != -1:
+            raise ValueError("a workspace goes with the automatic tile (tile=-1)")
+        _same_device(xq, workspace)
+        wp, wb = _workspace(workspace)
+        with torch.cuda.device(xq.device):
+            call("int8_scaled_mm_ws", xq.data_ptr(), _ld(xq), ptr(xs), w_packed.data_ptr(), ptr(ws),
+                 ptr(bias), M, N, K, mode, out.data_ptr(), _ld(out), wp, wb, _stream(xq))
+        return out
     with torch.cuda.device(xq.device):
         call("int8_scaled_mm_tile", xq.data_ptr(), _ld(xq), ptr(xs), w_packed.data_ptr(), ptr(ws),
              ptr(bias), M, N, K, mode, out.data_ptr(), _ld(out), _stream(xq), tile)
@@ -210,13 +247,15 @@ def scaled_mm(xq: torch.Tensor, xs: Optional[torch.Tensor], w_packed: torch.Tens
 def quant_scaled_mm(x: torch.Tensor, w_packed: torch.Tensor, ws: Optional[torch.Tensor], N: int,
                     bias: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
                     out: Optional[torch.Tensor] = None, tile: int = -1,
-                    xq: Optional[torch.Tensor] = None, xs: Optional[torch.Tensor] = None
+                    xq: Optional[torch.Tensor] = None, xs: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None
                     ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Per-token quant of bf16 or fp16 x [M, K] and the scaled matmul in one call.
 
     out_dtype defaults to x's type. Returns (out, xq, xs): out as scaled_mm
     returns it, and the int8 codes and fp32 scales the quant produced
-    (bit-identical to quant_per_token)."""
+    (bit-identical to quant_per_token). A workspace (bf16 x, automatic tile)
+    lets decode-shaped products split K, as in scaled_mm."""
     _matrix(x, "x", _act_dtype(x))
     if out_dtype is None:
         out_dtype = x.dtype
@@ -245,6 +284,16 @@ def quant_scaled_mm(x: torch.Tensor, w_packed: torch.Tensor, ws: Optional[torch.
         return None if t is None or mode == W8A8_OUT_I32 else t.data_ptr()
 
     _same_device(x, w_packed, xq, xs, out, *((ws, bias) if mode != W8A8_OUT_I32 else ()))
+    if workspace is not None:
+        if tile != -1 or x.dtype != torch.bfloat16:
+            raise ValueError("a workspace goes with bf16 activations and the automatic tile")
+        _same_device(x, workspace)
+        wp, wb = _workspace(workspace)
+        with torch.cuda.device(x.device):
+            call("int8_quant_scaled_mm_ws", x.data_ptr(), _ld(x), xq.data_ptr(), _ld(xq),
+                 xs.data_ptr(), w_packed.data_ptr(), ptr(ws), ptr(bias), M, N, K, mode,
+                 out.data_ptr(), _ld(out), wp, wb, _stream(x))
+        return out, xq, xs
     with torch.cuda.device(x.device):
         call("int8_quant_scaled_mm" + _ACT_ENTRY[x.dtype] + "_tile", x.data_ptr(), _ld(x),
              xq.data_ptr(), _ld(xq), xs.data_ptr(), w_packed.data_ptr(), ptr(ws), ptr(bias), M,
