@@ -31,9 +31,9 @@
  *   - Calls are thread-safe. Shared host state is atomic: per-device caches
  *     (the "is this a gfx950" answer, the fused kernels' resident-workgroup
  *     capacity) and a per-device launch counter for the fused kernels'
- *     flags; the error message is thread-local. The only library-owned
- *     device memory is those flags, a static array (see
- *     int8_quant_scaled_mm).
+ *     flags; the error message is thread-local. The library-owned device
+ *     memory is static: those flags (see int8_quant_scaled_mm) and the
+ *     workspace of int8_quant_scaled_mm_noalloc.
  */
 #ifndef W8A8_H
 #define W8A8_H
@@ -310,6 +310,28 @@ w8a8_status_t int8_quant_scaled_mm_ws(const uint16_t *x, int64_t ldx, int8_t *xq
                                       const uint16_t *bias, int64_t M, int64_t N, int64_t K,
                                       int mode, void *out, int64_t ldo, void *workspace,
                                       size_t workspace_bytes, void *stream);
+
+/*
+ * int8_quant_scaled_mm_noalloc - int8_quant_scaled_mm_ws for callers that
+ * cannot allocate device memory (code under graph capture, tight serving
+ * loops, harnesses that forbid allocation): the workspace is the library's
+ * own, a static device array of 4 MiB that each GPU holds from the
+ * library's first use until the process ends. The call allocates nothing
+ * (no hipMalloc, no allocating library routine); the caller still passes
+ * inputs and outputs.
+ *
+ * Shapes whose split needs more than 4 MiB of workspace
+ * (int8_scaled_mm_workspace_bytes) are W8A8_ERR_SHAPE. All calls on one GPU
+ * share that GPU's array: its per-tile words start at zero and every call
+ * leaves them zero, but calls that overlap on one GPU (two streams, or
+ * concurrent graph replays) race and must be serialized by the caller.
+ * Other requirements and errors: those of int8_quant_scaled_mm.
+ */
+w8a8_status_t int8_quant_scaled_mm_noalloc(const uint16_t *x, int64_t ldx, int8_t *xq,
+                                           int64_t ldq, float *x_scale, const void *w_packed,
+                                           const float *w_scale, const uint16_t *bias, int64_t M,
+                                           int64_t N, int64_t K, int mode, void *out, int64_t ldo,
+                                           void *stream);
 
 /*
  * int8_quant_scaled_mm_f16 - int8_quant_scaled_mm for fp16 activations x

@@ -46,6 +46,8 @@ SIGNATURES = {
                                  _vp, ctypes.c_size_t, _vp]),
     "int8_quant_scaled_mm_ws": (_int, [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
                                        _int, _vp, _i64, _vp, ctypes.c_size_t, _vp]),
+    "int8_quant_scaled_mm_noalloc": (_int, [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64,
+                                            _i64, _int, _vp, _i64, _vp]),
     "int8_quant_scaled_mm_f16": (_int, [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
                                         _int, _vp, _i64, _vp]),
     "int8_quant_scaled_mm_f16_tile": (_int, [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64,

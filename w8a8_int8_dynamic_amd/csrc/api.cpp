@@ -474,6 +474,41 @@ W8A8_API w8a8_status_t int8_quant_scaled_mm_ws(const uint16_t *x, int64_t ldx, i
                            workspace_bytes);
 }
 
+W8A8_API w8a8_status_t int8_quant_scaled_mm_noalloc(const uint16_t *x, int64_t ldx, int8_t *xq,
+                                                    int64_t ldq, float *x_scale,
+                                                    const void *w_packed, const float *w_scale,
+                                                    const uint16_t *bias, int64_t M, int64_t N,
+                                                    int64_t K, int mode, void *out, int64_t ldo,
+                                                    void *stream)
+{
+    const char *what = "int8_quant_scaled_mm_noalloc";
+    const size_t need = int8_scaled_mm_workspace_bytes(M, N, K);
+    if (need > w8a8::kScratchBytes)
+        return fail(W8A8_ERR_SHAPE,
+                    "%s: this shape's split needs %zu bytes of workspace, more than the %zu "
+                    "the library holds",
+                    what, need, w8a8::kScratchBytes);
+    void *scratch = nullptr;
+    if (need > 0 && M > 0) {
+        // Argument errors are reported before any HIP call.
+        w8a8::MmArgs a;
+        int t;
+        w8a8_status_t st = mm_args(xq, ldq, x_scale, w_packed, w_scale, bias, M, N, K, mode, out,
+                                   ldo, -1, true, what, a, t);
+        if (st != W8A8_OK)
+            return st;
+        st = check_device();
+        if (st != W8A8_OK)
+            return st;
+        hipError_t err = w8a8::scratch_address(&scratch);
+        if (err != hipSuccess)
+            return fail(W8A8_ERR_HIP, "%s: the library's workspace has no device address: %s", what,
+                        hipGetErrorString(err));
+    }
+    return quant_mm_common(x, w8a8::kElemBF16, ldx, xq, ldq, x_scale, w_packed, w_scale, bias, M,
+                           N, K, mode, out, ldo, stream, -1, what, scratch, w8a8::kScratchBytes);
+}
+
 W8A8_API w8a8_status_t int8_scaled_mm(const int8_t *xq, int64_t ldq, const float *x_scale,
                                       const void *w_packed, const float *w_scale,
                                       const uint16_t *bias, int64_t M, int64_t N, int64_t K,

@@ -91,6 +91,11 @@ struct SkinnySplit {
 };
 SkinnySplit skinny_split(int64_t tiles, int fm, int fn, int wk, int kblocks);
 
+// The library's own workspace for callers that cannot allocate: a static
+// device array of kScratchBytes per device (skinny_mm.hip). *ptr is its
+// device address on the current device, looked up once per device.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+hipError_t scratch_address(void **ptr);
 
 // Output kinds, the ABI's W8A8_OUT_* values: they index TileEntry's kernels.
 constexpr int kOutBF16 = 0, kOutI32 = 1, kOutF16 = 2, kOutKinds = 3;

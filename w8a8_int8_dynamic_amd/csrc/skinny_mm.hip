@@ -37,6 +37,7 @@
 // fragments past N read the last fragment, token chunks past K read the last
 // chunk (which meets zero weights); stores are masked.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "internal.hpp"
@@ -516,6 +517,35 @@ hipError_t launch_skinny_quant_mm(const MmArgs &a, const TileEntry &e, int mode,
     hipLaunchKernelGGL(e.fused[mode], dim3((unsigned)tiles), dim3(e.threads),
                        lds, stream, a);
     return hipGetLastError();
+}
+
+// The workspace of int8_quant_scaled_mm_noalloc: the split counters
+// (zero when the code object loads; every call leaves them zero) and the
+// partial sums. Host code never passes this name to a kernel: it is a
+// host-side stand-in, and scratch_address() gives the device address.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(void **ptr)
+{
+    constexpr int kDevices = 64;
+    static std::mutex lock;
+    static void *addr[kDevices];
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return err;
+    if (dev < 0 || dev >= kDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> guard(lock);
+    if (addr[dev] == nullptr) {
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess)
+            return err;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 SkinnySplit skinny_split(int64_t tiles, int fm, int fn, int wk, int kblocks)
