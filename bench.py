@@ -50,6 +50,8 @@ def parse_args(argv=None):
                    help="target wall time of the oracle's sampled GEMM")
     p.add_argument("--no-quant-large", action="store_true",
                    help="skip the quant bandwidth run on the FFN-down activations")
+    p.add_argument("--hw-probes", action="store_true",
+                   help="run the memory-path probes (tests/probes/hw_probes) and print their results")
     p.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV", default=None,
                    help="print the summary of a rocprofv3 kernel trace of a bench run (no GPU)")
     p.add_argument("--no-workloads", action="store_true",
@@ -490,6 +492,18 @@ def trace_summary(path: str) -> str:
 
 def main(argv=None) -> int:
     args = parse_args(argv)
+    if args.hw_probes:
+        import subprocess
+        exe = os.path.join(ROOT, "tests", "probes", "hw_probes")
+        if not os.path.exists(exe):
+            print("tests/probes/hw_probes is not built (__graft_entry__.build())", file=sys.stderr)
+            return 1
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+        if r.returncode != 0:
+            print(r.stderr, file=sys.stderr)
+            return r.returncode
+        print(json.dumps({"hw_probes": [json.loads(l) for l in r.stdout.splitlines() if l.strip()]}))
+        return 0
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
         return 0

@@ -69,6 +69,26 @@ def build(jobs: int = 4, save_temps: bool = False, verbose: bool = False) -> str
     return LIBRARY
 
 
+PROBES_SOURCE = os.path.join(ROOT, "tests", "probes", "hw_probes.cpp")
+PROBES_BINARY = os.path.join(ROOT, "tests", "probes", "hw_probes")
+
+
+def build_probes(verbose: bool = False) -> str:
+    """Compile the memory-path probes (tests/probes/hw_probes.cpp, measurement
+    infrastructure run by `bench.py --hw-probes`, not part of the library)."""
+    tmp = PROBES_BINARY + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-x", "hip",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           PROBES_SOURCE, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling the probes failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBES_BINARY)
+    if verbose:
+        print(f"built {PROBES_BINARY}")
+    return PROBES_BINARY
+
+
 def main(argv=None) -> int:
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--jobs", type=int, default=min(4, os.cpu_count() or 1))
