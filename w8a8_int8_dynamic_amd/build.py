@@ -1,6 +1,6 @@
 """Build libw8a8.so (HIP for gfx950) in-tree with hipcc.
 
-    python w8a8_int8_dynamic_amd/build.py [--jobs N] [--save-temps]
+    python w8a8_int8_dynamic_amd/build.py [--jobs N] [--save-temps] [--no-timeline]
 
 (run as a script, or through __graft_entry__.build(): importing the package
 loads the library, which may not exist yet)
@@ -8,7 +8,11 @@ loads the library, which may not exist yet)
 Each source is compiled to an object under ``_build/`` in parallel, then
 linked into ``w8a8_int8_dynamic_amd/libw8a8.so``. Floating-point flags are
 fixed: no fast-math, no contraction (the epilogue's rounding order is part
-of the result), and packed-fp32 instructions disabled.
+of the result), and packed-fp32 instructions disabled. By default the
+measurement twin ``libw8a8_timeline.so`` is linked too: the same objects
+with scaled_mm.hip compiled once more with W8A8_TIMELINE (per-workgroup
+phase stamps of the main kernel, read by tests/probes/fused_timeline.py).
+Nothing in the package loads it.
 """
 from __future__ import annotations
 
@@ -24,6 +28,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIBRARY = os.path.join(HERE, "libw8a8.so")
+# The measurement twin: the same objects but scaled_mm.hip compiled with
+# W8A8_TIMELINE (per-workgroup phase stamps of the main kernel, timeline.hpp).
+TIMELINE_LIBRARY = os.path.join(HERE, "libw8a8_timeline.so")
+TIMELINE_SOURCE = "scaled_mm.hip"
 SOURCES = ["quant.hip", "prepack.hip", "scaled_mm.hip", "scaled_mm_fp8.hip", "skinny_mm.hip", "api.cpp"]
 ARCH = "gfx950"
 
@@ -43,8 +51,8 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, extra, tag: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + tag + ".o")
     cmd = [hipcc(), *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD)
     if r.returncode != 0:
@@ -52,20 +60,34 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(jobs: int = 4, save_temps: bool = False, verbose: bool = False) -> str:
-    """Compile every source and link libw8a8.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    extra = ["-save-temps"] if save_temps else []
-    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIBRARY + ".tmp"
+def _link(objs, library: str) -> None:
+    tmp = library + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"linking libw8a8.so failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIBRARY)
+        raise RuntimeError(f"linking {os.path.basename(library)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, library)
+
+
+def build(jobs: int = 4, save_temps: bool = False, verbose: bool = False,
+          timeline: bool = True) -> str:
+    """Compile every source and link libw8a8.so (and, with timeline, its
+    measurement twin libw8a8_timeline.so); returns the library path."""
+    os.makedirs(BUILD, exist_ok=True)
+    extra = ["-save-temps"] if save_temps else []
+    jobs_list = [(s, extra, "") for s in SOURCES]
+    if timeline:
+        jobs_list.append((TIMELINE_SOURCE, ["-DW8A8_TIMELINE"], ".timeline"))
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs_list))
+    _link(objs[:len(SOURCES)], LIBRARY)
     if verbose:
         print(f"built {LIBRARY}")
+    if timeline:
+        twin = [o for o in objs[:len(SOURCES)] if not o.endswith(TIMELINE_SOURCE + ".o")]
+        _link(twin + [objs[-1]], TIMELINE_LIBRARY)
+        if verbose:
+            print(f"built {TIMELINE_LIBRARY}")
     return LIBRARY
 
 
@@ -93,8 +115,10 @@ def main(argv=None) -> int:
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--jobs", type=int, default=min(4, os.cpu_count() or 1))
     p.add_argument("--save-temps", action="store_true")
+    p.add_argument("--no-timeline", action="store_true",
+                   help="skip the measurement twin libw8a8_timeline.so")
     args = p.parse_args(argv)
-    build(args.jobs, args.save_temps, verbose=True)
+    build(args.jobs, args.save_temps, verbose=True, timeline=not args.no_timeline)
     return 0
 
 

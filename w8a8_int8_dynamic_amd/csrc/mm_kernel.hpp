@@ -55,6 +55,7 @@
 #include "fused_rows.hpp"
 #include "internal.hpp"
 #include "quant_rule.hpp"
+#include "timeline.hpp"
 
 namespace w8a8 {
 namespace {
@@ -220,6 +221,7 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
     using Acc = std::conditional_t<FP8, v16f, v16i>;
     constexpr int IN = OUT_F16 ? kElemF16 : kElemBF16;
     __shared__ uint4 lds[T::LDS / 16];
+    W8A8_STAMP(0);
 
     MmArgs a;
     a.xq = pinned_ptr(args.xq);
@@ -492,7 +494,9 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
         const int r0 = (int)blockIdx.x * a.rows_per_wg;
         const int r1 = min(r0 + a.rows_per_wg, a.M);
         fused::quantize_rows<T::THREADS, IN, FP8>(a, r0, r1, red);
+        W8A8_STAMP(1);
         fused::publish(a, r0 < r1);
+        W8A8_STAMP(2);
         const int rows = min(T::BM, a.M - m0);
         const int producers = (rows + a.rows_per_wg - 1) / a.rows_per_wg;
         if (fused::wait_producers(a, m0 / a.rows_per_wg, producers, decision)) {
@@ -501,6 +505,8 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
             __syncthreads();
         }
     }
+
+    W8A8_STAMP(3);
 
     // Scales (and bias) of the tile, fetched now into a couple of registers
     // per thread and parked in LDS for the epilogue, so that their latency
@@ -559,6 +565,8 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
     if constexpr (T::WLDS)
         bread(0, bf[0]);
 
+    W8A8_STAMP(4);
+
     // Steady state: GROUP unconditional steps while every stage they fetch
     // exists.
     int s0 = 0;
@@ -572,6 +580,8 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
         if (s0 + decltype(U)::value < S)
             step(Part{}, s0 + decltype(U)::value, U);
     });
+
+    W8A8_STAMP(5);
 
     // ---- epilogue ----
     // Accumulator layout: acc[j][i] register 4q+r of lane l holds channel
@@ -762,6 +772,7 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
         if (wk == decltype(W)::value)
             epilogue(W);
     });
+    W8A8_STAMP(6);
 }
 
 // The main kernel's tile configurations in tile-number order (the int8

@@ -209,3 +209,16 @@ hipError_t launch_quant_scaled_mm_entry(MmArgs a, int mode, const TileEntry &e, 
 }
 
 }  // namespace w8a8
+
+#ifdef W8A8_TIMELINE
+// Measurement builds only (libw8a8_timeline.so): copies the first `bytes`
+// bytes of the int8 kernels' timeline records (timeline.hpp) on the current
+// device to host memory `dst`, synchronously; returns the hipError_t.
+extern "C" __attribute__((visibility("default"))) int w8a8_timeline_read(void *dst, size_t bytes)
+{
+    if (bytes > sizeof(w8a8::timeline::g_stamp))
+        return (int)hipErrorInvalidValue;
+    return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(w8a8::timeline::g_stamp), bytes, 0,
+                                    hipMemcpyDeviceToHost);
+}
+#endif
