@@ -62,6 +62,8 @@ def main(argv=None) -> int:
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("workload", nargs="?", default="fused_qkv")
     p.add_argument("--reps", type=int, default=300)
+    p.add_argument("--save", metavar="DIR", default=None,
+                   help="also write each form's raw records (uint64 [workgroups, 16]) as .npy")
     args = p.parse_args(argv)
 
     import torch
@@ -127,6 +129,10 @@ def main(argv=None) -> int:
         assert err == 0, err
         rec = {"form": label}
         rec.update(summarize(buf.reshape(grid, SLOTS), label == "int8_quant_scaled_mm"))
+        if args.save:
+            os.makedirs(args.save, exist_ok=True)
+            np.save(os.path.join(args.save, f"timeline_{args.workload}_{label}.npy"),
+                    buf.reshape(grid, SLOTS))
         print(json.dumps(rec), flush=True)
     for label, fn in (("int8_quant_scaled_mm", fused), ("int8_scaled_mm", plain)):
         for _ in range(50):
