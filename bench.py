@@ -10,7 +10,9 @@ grid fits the device, else the two kernels back to back). The weight is
 quantized per output channel and repacked once, before timing. Inputs are
 seeded synthetic tensors (workloads/), already resident in HBM when the
 timed region starts. After the --warmup steps the step keeps running,
-untimed, for 0.3 s so that the timed loops start at steady clocks.
+untimed, for 0.3 s so that the timed loops start at steady clocks. The
+default of 2000 timed steps (about 70 ms) averages over the part's power
+management, which moves 200-step loops of the same step by up to 10 %.
 
 Printed: one JSON line with the step throughput (int8 TOP/s of 2*M*N*K per
 step), the same step as two separate calls, the roofline of the matmul
@@ -41,7 +43,8 @@ PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E, GB/s
 def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--steps", type=int, default=2000,
+                   help="timed steps (2000: about 70 ms of back-to-back steps on the default workload; 200-step loops vary by up to 10 %% with the part's power state)")
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="fused_qkv")
     p.add_argument("--tile", type=int, default=-1, help="force a matmul tile id (-1 = automatic)")

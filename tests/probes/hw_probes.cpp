@@ -13,6 +13,10 @@
 //   hbm_floor   back-to-back launches that each read S bytes once from HBM
 //               (rotating over buffers larger than the last-level cache):
 //               the time one streaming kernel of that size takes.
+//   mfma_only   the fused-QKV matmul's MFMA work with no memory traffic: 256
+//               workgroups of 4 waves, each wave 768 v_mfma_i32_32x32x32_i8
+//               on 12 accumulators (and 16 times that), back to back, with
+//               the shader clock read inside the kernel.
 //
 // Every global index is taken modulo a power-of-two window inside its
 // buffer and every LDS index modulo the array, so no access leaves its
@@ -94,6 +98,42 @@ __global__ __launch_bounds__(256) void floor_kernel(const v4i *buf, size_t n16, 
         acc += buf[i];
     if (acc[0] == 0x7fffffff && acc[1] == 12345)
         out[blockIdx.x & 1023] = acc[2];
+}
+
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// Each wave runs `steps` rounds of 12 independent MFMAs (one per
+// accumulator, as a 128 x 192 tile's wave does per 32-deep k-step). Thread 0
+// of workgroup 0 writes s_memtime and s_memrealtime at its start and end to
+// clk[0..3].
+__global__ __launch_bounds__(256) void mfma_kernel(int steps, int *out, long long *clk)
+{
+    const long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    const int lane = threadIdx.x & 63;
+    v4i a = {lane, lane * 3, lane * 5, lane * 7};
+    v4i b = {lane * 11, lane * 13, lane ^ 17, lane ^ 19};
+    v16i acc[12];
+#pragma unroll
+    for (int i = 0; i < 12; ++i)
+        acc[i] = v16i{};
+    for (int s = 0; s < steps; ++s) {
+#pragma unroll
+        for (int i = 0; i < 12; ++i)
+            acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[i], 0, 0, 0);
+        a += 1;
+    }
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 12; ++i)
+        sum += acc[i][0] + acc[i][15];
+    if (sum == 0x7fffffff)
+        out[blockIdx.x & 1023] = sum;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        clk[0] = t0;
+        clk[1] = r0;
+        clk[2] = __builtin_amdgcn_s_memtime();
+        clk[3] = __builtin_amdgcn_s_memrealtime();
+    }
 }
 
 template <class F>
@@ -184,6 +224,23 @@ int main()
         for (auto &p : b)
             CHECK(hipFree(p));
     }
+    long long *clk;
+    CHECK(hipMalloc(&clk, 4 * sizeof(long long)));
+    for (int mult : {1, 16}) {
+        const int steps = 64 * mult;              // 12 * 64 = 768 MFMAs per wave at 1x
+        auto launch = [&](int) {
+            hipLaunchKernelGGL(mfma_kernel, dim3(cus), dim3(256), 0, 0, steps, out, clk);
+        };
+        const double us = time_us(launch, 100);
+        long long c[4];
+        CHECK(hipMemcpy(c, clk, sizeof(c), hipMemcpyDeviceToHost));
+        const double ops = (double)cus * 4 * steps * 12 * (2.0 * 32 * 32 * 32);
+        printf("{\"probe\": \"mfma_only\", \"workgroups\": %d, \"mfma_per_wave\": %d, "
+               "\"us_per_launch\": %.2f, \"pops\": %.3f, \"sclk_ghz\": %.3f}\n",
+               cus, steps * 12, us, ops / (us * 1e-6) / 1e15,
+               (double)(c[2] - c[0]) / ((double)(c[3] - c[1]) * 10.0));
+    }
+    CHECK(hipFree(clk));
     CHECK(hipFree(out));
     return 0;
 }
