@@ -49,18 +49,23 @@ const char *mm_tile_name(int tile)
 }
 
 // Automatic choice: the smallest modelled time (rates measured on MI355X
-// under full load).
-//   Main kernel: a tile costs the larger of its MFMA time and the time to
-//   stream its operands from L2, plus a fixed cost (prologue and epilogue);
-//   tiles run in full-machine rounds of one workgroup per CU. About 16000
-//   int8 MFMA ops per ns per CU (the shader clock drops to ~2 GHz) and about
-//   80 bytes per ns of L2 reads per CU (~20 TB/s in all).
+// under full load). Workgroups run in rounds of one per CU (256 CUs).
+//   Main kernel: a tile costs the largest of its MFMA time, the time to
+//   stream its operands from L2 and, where few row tiles share its weight
+//   columns (small M), the time to stream its weight columns from HBM, plus
+//   a fixed cost (prologue and epilogue). About 16000 int8 MFMA ops per ns
+//   per CU (the shader clock drops to ~2 GHz), about 80 bytes per ns of L2
+//   reads per CU (~20 TB/s in all), and about 22 bytes per ns per CU from
+//   HBM for its four waves; the row tiles of one band (up to 4) share each
+//   weight fetch.
 //   Small-M kernel, for up to 32 token rows (beyond that each weight byte
 //   meets enough tokens for the main kernel's tiles): the weight stream, at
-//   about 38 bytes per ns from HBM per busy CU (each row tile streams the
-//   whole weight), or the L2 reads of the workgroups if more: each k-block
-//   brings the weight fragments and one 128-byte line per token row, ~14
-//   TB/s in all; plus a fixed cost.
+//   about 38 bytes per ns from HBM per busy CU, in rounds (each tile streams
+//   its BN weight columns over all of K), or the L2 reads of all workgroups
+//   if more: each k-block brings the weight fragments and one 128-byte line
+//   per token row, ~16 TB/s in all; plus a fixed cost. Fitted on MI355X to
+//   the measured best tile of nine decode shapes (M 1-32, N 3072-12288, K
+//   4096-12288, weights streamed from HBM), all within 0.5 % of the best.
 int mm_tile_auto(int64_t M, int64_t N, int64_t K)
 {
     const double cus = 256.0;
@@ -73,17 +78,17 @@ int mm_tile_auto(int64_t M, int64_t N, int64_t K)
             continue;
         const int64_t tiles_m = ceil_div(M, e.bm);
         const int64_t tiles = tiles_m * ceil_div(N, e.bn);
+        const double rounds = std::ceil((double)tiles / cus);
         double cost;
         if (!e.skinny) {
-            const double rounds = std::ceil((double)tiles / cus);
             const double t_mma = 2.0 * e.bm * e.bn * kk / 16000.0;
             const double t_l2 = (double)(e.bm + e.bn) * kk / 80.0;
-            cost = rounds * (std::max(t_mma, t_l2) + 3000.0);
+            const double t_hbm = (double)e.bn * kk / (double)std::min<int64_t>(tiles_m, 4) / 22.0;
+            cost = rounds * (std::max({t_mma, t_l2, t_hbm}) + 3000.0);
         } else {
-            const double weight = (double)tiles_m * (double)round_up(N, 16) * kk;
-            const double t_hbm = weight / (std::min((double)tiles, cus) * 38.0);
+            const double t_hbm = rounds * (double)e.bn * kk / 38.0;
             const double rows = (double)std::min<int64_t>(M, e.bm);
-            const double t_l2 = (double)tiles * kblocks * (e.bn / 16 * 1024.0 + rows * 128.0) / 14000.0;
+            const double t_l2 = (double)tiles * kblocks * (e.bn / 16 * 1024.0 + rows * 128.0) / 16000.0;
             cost = std::max(t_hbm, t_l2) + 3000.0;
         }
         if (cost < best_cost * 0.999) {

@@ -363,6 +363,7 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             __builtin_amdgcn_s_waitcnt(0);             // every store above has completed
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);   // and the compiler keeps them above
             if (lane == 0)
                 __hip_atomic_fetch_add(words + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return;
@@ -370,6 +371,7 @@ __global__ __launch_bounds__(S::THREADS, 1024 / S::THREADS) void skinny_mm_kerne
         while (__hip_atomic_load(words + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
                (unsigned)(nsplit - 1))
             __builtin_amdgcn_s_sleep(1);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);       // no partial load moves above the wait
 #pragma unroll 1
         for (int o = 0; o < nsplit; ++o) {
             if (o == ks)
