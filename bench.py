@@ -457,8 +457,9 @@ def accuracy_record(torch, ops, wl) -> dict:
 def trace_summary(path: str) -> str:
     """Summary of a rocprofv3 kernel trace (its kernel_trace.csv) of a bench
     run: per kernel, the dispatch count and mean / min / max duration, over
-    the whole run and over the timed step loop alone (the dispatches between
-    the two bitwise_not marker launches that bracket it), with the loop's
+    the whole run, over the timed step loop alone (the dispatches between
+    the first two bitwise_not marker launches) and over the roofline's
+    matmul loop (between the third and fourth), with each loop's
     start-to-start period. Markdown text."""
     import csv
     rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
@@ -480,13 +481,15 @@ def trace_summary(path: str) -> str:
         return out
 
     lines = table(rows, "All dispatches of the run:")
-    if len(marks) >= 2:
-        loop = rows[marks[0] + 1:marks[1]]
+    for a, b, what in ((0, 1, "timed step loop"), (2, 3, "roofline's matmul loop")):
+        if len(marks) <= b:
+            break
+        loop = rows[marks[a] + 1:marks[b]]
         starts = [int(r["Start_Timestamp"]) for r in loop]
         ends = [int(r["End_Timestamp"]) for r in loop]
-        lines += [""] + table(loop, "The timed step loop (between the markers):")
+        lines += [""] + table(loop, f"The {what} (between markers {a + 1} and {b + 1}):")
         if len(loop) > 1:
-            lines += ["", f"Timed step loop: {len(loop)} dispatches, first start to last end "
+            lines += ["", f"{what[0].upper() + what[1:]}: {len(loop)} dispatches, first start to last end "
                           f"{(ends[-1] - starts[0]) / 1e3:.3f} us, "
                           f"{(ends[-1] - starts[0]) / 1e3 / len(loop):.3f} us per dispatch; mean "
                           f"start-to-start period {(starts[-1] - starts[0]) / 1e3 / (len(loop) - 1):.3f} us."]
@@ -598,7 +601,9 @@ def main(argv=None) -> int:
     ms_step = time_loop(torch, step, args.steps)
     torch.bitwise_not(marker, out=marker)
     ms_step2 = time_loop(torch, step_two_calls, args.steps)
+    torch.bitwise_not(marker, out=marker)      # the matmul loop of the roofline: markers 3 and 4
     ms_mm = time_loop(torch, mm, args.steps)
+    torch.bitwise_not(marker, out=marker)
     ms_quant = time_loop(torch, quant, args.steps)
     each = {name: time_each(torch, fn, min(args.steps, 100))
             for name, fn in (("step", step), ("mm", mm), ("quant", quant))}
