@@ -58,6 +58,25 @@ def test_only_the_abi_is_exported():
     assert text_syms <= set(declared_functions()), text_syms - set(declared_functions())
 
 
+def test_timeline_twin_exports_the_abi_and_its_reader():
+    """The measurement twin (libw8a8_timeline.so, built beside the library)
+    exports the same entry points plus w8a8_timeline_read; the library proper
+    has no trace of the timeline."""
+    twin = os.path.join(os.path.dirname(_lib.LIBRARY), "libw8a8_timeline.so")
+    if not os.path.exists(twin):
+        pytest.skip("libw8a8_timeline.so not built")
+
+    def text_syms(path):
+        out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                             check=True).stdout
+        return {line.split()[-1] for line in out.splitlines()
+                if len(line.split()) == 3 and line.split()[1] == "T"}
+
+    lib, tw = text_syms(_lib.LIBRARY), text_syms(twin)
+    assert tw == lib | {"w8a8_timeline_read"}
+    assert "w8a8_timeline_read" not in lib
+
+
 def test_constants_match_header():
     text = open(HEADER).read()
     assert f"#define W8A8_MAX_K {_lib.W8A8_MAX_K}" in text
