@@ -515,7 +515,7 @@ def main(argv=None) -> int:
         return 0
     if args.gpus != 1 or world_size() != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
-              f"{world_size()}); this build has no multi-GPU path.", file=sys.stderr)
+              f"{world_size()}); the library has no multi-GPU path.", file=sys.stderr)
         return 2
 
     import torch
