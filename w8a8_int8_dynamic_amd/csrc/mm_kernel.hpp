@@ -156,11 +156,14 @@ constexpr int clcm(int a, int b) { return a / cgcd(a, b) * b; }
 // LW stages ahead of their use. WL: the weights go through LDS as well (in
 // the token pipeline, LT stages ahead of their LDS write), so that row
 // groups sharing a weight fragment (WM = 2) fetch it once; LW is then
-// unused.
-template <int BM_, int BN_, int WM_, int WN_, int WK_, int LT_, int LW_, bool WL_ = false>
+// unused. MP: memory instructions placed after each MFMA of a step's
+// interleave (int8; the e4m3 twin spreads them evenly over its MFMAs).
+template <int BM_, int BN_, int WM_, int WN_, int WK_, int LT_, int LW_, bool WL_ = false,
+          int MP_ = 1>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, WK = WK_, LT = LT_, LW = LW_;
     static constexpr bool WLDS = WL_;
+    static constexpr int MP = MP_;
     static constexpr int NW = WM * WN * WK;            // wavefronts per workgroup
     static constexpr int THREADS = NW * 64;
     static constexpr int MB = BM / 16;                 // 16-row token images per k-block
@@ -407,13 +410,15 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
     };
     constexpr int NMMA = (FP8 ? 1 : 2) * T::FN * T::FM;   // MFMAs per wave per stage
     constexpr int PRE = FP8 ? 1 : 2;                   // of them issued before the barrier
-    // Memory instructions placed after each MFMA of the interleave: one for
-    // int8; the e4m3 twin has half as many (twice as long) MFMAs, so its
-    // memory instructions are spread over them.
+    // Memory instructions placed after each MFMA of the interleave: the
+    // tile's MP for int8 (one where a step has about as many memory
+    // instructions as MFMAs; two or three on the tiles with two or three
+    // times as many, measured on MI355X); the e4m3 twin has half as many
+    // (twice as long) MFMAs, so its memory instructions are spread over them.
     constexpr int DS_READS = 2 * T::FM + (T::WLDS ? 2 * T::FN : 0);
     constexpr int DS_WRITES = T::LA + T::LW8;
     constexpr int MEM_OPS = DS_READS + DS_WRITES + T::LPW;
-    constexpr int PER = FP8 ? (MEM_OPS + NMMA - PRE - 1) / (NMMA - PRE) : 1;
+    constexpr int PER = FP8 ? (MEM_OPS + NMMA - PRE - 1) / (NMMA - PRE) : T::MP;
 
     // Step s. On entry stage s+1 is being written to LDS by every wave, this
     // wave's operands of stage s are in xf[s & 1], token rows of stage s+2
@@ -422,7 +427,7 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
     // core busy across the barrier), barrier (stage s+1 visible; every read
     // of stage s done), read stage s+1's operands, write stage s+2 to the LDS
     // buffer stage s used, fetch tokens of stage s+2+LT and weights of stage
-    // s+LW, interleaved one by one with the rest of stage s's MFMAs so that
+    // s+LW, interleaved (PER at a time) with the rest of stage s's MFMAs so that
     // they issue while the matrix core is busy.
     auto step = [&](auto full, int s, auto u_c) __attribute__((always_inline)) {
         constexpr bool FULL = decltype(full)::value;
@@ -460,7 +465,7 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
         if (run)
             mma(std::integral_constant<int, PRE>{}, std::integral_constant<int, NMMA>{}, xf[u & 1], wcur);
         if (FULL) {
-            // One memory instruction after each MFMA: operand reads first,
+            // PER memory instructions after each MFMA: operand reads first,
             // then the LDS writes, then the global loads.
             static_for<(DS_READS + PER - 1) / PER>([&](auto) __attribute__((always_inline)) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
@@ -781,9 +786,9 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
 // leads in stages ("l2lds": weights through LDS in the token pipeline, two
 // stages ahead; measured on MI355X 6-9 % faster than fetching them straight
 // into registers, where the two row groups each load every fragment).
-using MainTiles = std::tuple<Tile<64, 64, 1, 2, 2, 2, 3>, Tile<64, 128, 1, 2, 2, 2, 3>,
-                             Tile<128, 64, 1, 2, 2, 2, 3>, Tile<128, 128, 1, 2, 2, 2, 3>,
-                             Tile<128, 192, 1, 2, 2, 2, 3>, Tile<256, 128, 2, 2, 1, 2, 3, true>,
+using MainTiles = std::tuple<Tile<64, 64, 1, 2, 2, 2, 3>, Tile<64, 128, 1, 2, 2, 2, 3, false, 2>,
+                             Tile<128, 64, 1, 2, 2, 2, 3, false, 3>, Tile<128, 128, 1, 2, 2, 2, 3>,
+                             Tile<128, 192, 1, 2, 2, 2, 3>, Tile<256, 128, 2, 2, 1, 2, 3, true, 2>,
                              Tile<256, 192, 2, 2, 1, 2, 3, true>>;
 constexpr const char *kMainTileNames[] = {
     "64x64/m1n2k2/l23",   "64x128/m1n2k2/l23",    "128x64/m1n2k2/l23",    "128x128/m1n2k2/l23",
