@@ -69,6 +69,11 @@ typedef enum w8a8_mm_out {
  * codes (the quantizers only emit -127..127). */
 #define W8A8_MAX_K 131056
 
+/* Largest row pitch ldq (bytes) of the int8 (or e4m3) activation codes that
+ * the matmuls accept: the main kernel addresses a tile's 256 token rows with
+ * 32-bit offsets from the tile's first row. */
+#define W8A8_MAX_LDQ 4194304
+
 /*
  * int8_quant_per_token - dynamic per-token symmetric activation quantization.
  * (Page "Issue 5 probe ...", section "Round two": dynamic per-token symmetric
@@ -189,8 +194,9 @@ w8a8_status_t int8_unpack_weight(const void *w_packed, int64_t N, int64_t K, int
  * type (bf16 or fp16 bits) or NULL.
  * Output: bf16, fp16 or int32 [M, ldo].
  * Requirements: M >= 0 (M == 0 is a no-op), N >= 1, 16 <= K <= W8A8_MAX_K
- * with K a multiple of 16, ldq >= K, ldo >= N; xq and w_packed 16-byte
- * aligned, ldq a multiple of 16; out aligned to its element size. In I32
+ * with K a multiple of 16, K <= ldq <= W8A8_MAX_LDQ, ldo >= N; xq and
+ * w_packed 16-byte aligned, ldq a multiple of 16; out aligned to its element
+ * size. In I32
  * mode x_scale, w_scale and bias may be NULL and are ignored.
  * Errors: W8A8_ERR_SHAPE also when the tile's workgroups over M x N, times
  * its threads, do not fit in 32 bits (one launch's grid). That takes more
@@ -416,7 +422,7 @@ int w8a8_fp8_tile_count(void);
 int w8a8_fp8_tile_auto(int64_t M, int64_t N, int64_t K);
 
 /* Number of tile configurations, a short name of one, and the tile the
- * automatic choice picks for a shape. Main kernel: "128x192/m1n2k2/l23" is
+ * automatic choice picks for a shape. Main kernel: "128x192/m1n2k2/l33" is
  * tile rows x columns / wave row groups, column groups and k-groups / token
  * and weight fetch leads in stages. Small-M kernel (for a few token rows; the
  * automatic choice considers it up to 32 rows): "s16x32/k8/u4" is token rows

@@ -82,6 +82,10 @@ def test_constants_match_header():
     assert f"#define W8A8_MAX_K {_lib.W8A8_MAX_K}" in text
     assert 128 * 128 * _lib.W8A8_MAX_K < 2 ** 31 and _lib.W8A8_MAX_K % 16 == 0
     assert 128 * 128 * (_lib.W8A8_MAX_K + 16) >= 2 ** 31
+    # the main kernel's 32-bit offsets: 256 token rows of pitch ldq from a
+    # tile's first row
+    assert f"#define W8A8_MAX_LDQ {_lib.W8A8_MAX_LDQ}" in text
+    assert 256 * _lib.W8A8_MAX_LDQ + _lib.W8A8_MAX_K < 2 ** 31
 
 
 def test_status_strings():
@@ -182,6 +186,7 @@ def test_scaled_mm_validation():
     assert mm(K=0) == SHAPE and mm(K=8) == SHAPE and mm(K=72) == SHAPE
     assert mm(K=_lib.W8A8_MAX_K + 16, ldq=_lib.W8A8_MAX_K + 16) == SHAPE
     assert mm(ldq=48) == SHAPE and mm(ldo=15) == SHAPE
+    assert mm(ldq=_lib.W8A8_MAX_LDQ + 16) == SHAPE and mm(ldq=_lib.W8A8_MAX_LDQ) == DEVICE
     assert mm(M=0, xq=None, xs=None, wp=None, ws=None, out=None) == OK
     assert mm(xq=None) == NULL and mm(wp=None) == NULL and mm(out=None) == NULL
     assert mm(xs=None) == NULL and mm(ws=None) == NULL
@@ -208,6 +213,7 @@ def test_quant_scaled_mm_validation():
     # the matmul's own rules
     assert qmm(mode=3) == MODE and qmm(tile=-2) == MODE
     assert qmm(K=72) == SHAPE and qmm(ldq=48) == SHAPE and qmm(ldo=15) == SHAPE
+    assert qmm(ldq=_lib.W8A8_MAX_LDQ + 16) == SHAPE
     assert qmm(xq=None) == NULL and qmm(wp=None) == NULL and qmm(out=None) == NULL
     assert qmm(xq=A + 8) == ALIGN
     # the input rows
@@ -256,6 +262,7 @@ def test_fp8_entry_points_validation():
     # matmul
     assert fp8_mm(mode=3) == MODE and fp8_mm(tile=L.w8a8_fp8_tile_count()) == MODE
     assert fp8_mm(K=72) == SHAPE and fp8_mm(ldq=48) == SHAPE and fp8_mm(ldo=15) == SHAPE
+    assert fp8_mm(ldq=_lib.W8A8_MAX_LDQ + 16) == SHAPE and fp8_qmm(ldq=_lib.W8A8_MAX_LDQ + 16) == SHAPE
     assert fp8_mm(xq=None) == NULL and fp8_mm(ws=None) == NULL and fp8_mm(xs=None) == NULL
     assert fp8_mm(xq=A + 8) == ALIGN and fp8_mm(out=A + 1) == ALIGN
     assert fp8_mm(M=0, xq=None, xs=None, wp=None, ws=None, out=None) == OK

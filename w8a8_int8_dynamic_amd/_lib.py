@@ -22,6 +22,7 @@ W8A8_OUT_BF16 = 0
 W8A8_OUT_I32 = 1
 W8A8_OUT_F16 = 2
 W8A8_MAX_K = 131056
+W8A8_MAX_LDQ = 4194304
 
 # name -> (restype, argtypes), in the order of include/w8a8.h
 _i64, _vp, _int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int

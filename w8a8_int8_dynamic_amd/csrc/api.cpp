@@ -234,6 +234,8 @@ w8a8_status_t mm_args(const int8_t *xq, int64_t ldq, const float *x_scale, const
         return fail(W8A8_ERR_SHAPE, "%s: K must be a multiple of 16 in [16, %d]", what, W8A8_MAX_K);
     if (ldq < K || ldo < N)
         return fail(W8A8_ERR_SHAPE, "%s: leading dimension too small", what);
+    if (ldq > W8A8_MAX_LDQ)
+        return fail(W8A8_ERR_SHAPE, "%s: ldq above %d", what, W8A8_MAX_LDQ);
     a = w8a8::MmArgs{};
     t = -1;
     if (M == 0)

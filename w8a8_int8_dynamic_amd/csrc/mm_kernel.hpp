@@ -19,19 +19,21 @@
 //   - Four wavefronts split a BM x BN tile into WN column groups and WK
 //     k-groups: wave (wn, wk) owns all BM rows and BN/WN columns, and takes
 //     every WK-th 64-deep k-block. No weight fragment is used by two waves,
-//     so weights skip LDS entirely: each wave loads its operands straight
-//     from the prepacked weight into a ring of NS register sets (each load
-//     is 64 lanes x 16 bytes in four contiguous 256-byte runs).
+//     so weights skip LDS: each wave loads its operands straight from the
+//     prepacked weight into a ring of LW+1 register sets (each load is 64
+//     lanes x 16 bytes in four contiguous 256-byte runs).
 //   - Token rows are shared by the WN waves of a k-group, so they go
-//     through LDS: a ring of NS stages (WK k-blocks each). Every load is an
-//     ordinary global load the compiler tracks: token data is fetched NS-1
-//     stages ahead into a small register staging ring and written to LDS
-//     (ds_write_b128) one stage before use; one barrier per stage. (Direct
-//     global->LDS loads were tried: the compiler either drains them with a
-//     full vmcnt(0) before each LDS read, or, issued from inline asm, loses
-//     count of them and over-waits on the weight loads.)
+//     through LDS: a ring of LT+1 stages (WK k-blocks each), filled straight
+//     from memory by buffer_load_dwordx4 ... lds (no staging registers, no
+//     LDS write instructions), LT stages ahead of the operand reads; one
+//     barrier per stage. The MUBUF form of the LDS load matters: the
+//     compiler takes a FLAT-encoded one (global_load_lds) as possibly
+//     completing out of order and then turns every later wait into a full
+//     vmcnt(0). Against the earlier scheme (ordinary loads into registers,
+//     then ds_write_b128), measured on MI355X: 1.9 % faster on the
+//     fused-QKV shape, 5-6 % on the 256-row tiles, outputs bit-identical.
 //   - A 16-row x 64-k token image is loaded with lane 4r+j reading k-chunk
-//     j ^ swz(r) of row r and storing it to slot 4r+j: every 4-lane quad reads one row's 64 contiguous
+//     j ^ swz(r) of row r into slot 4r+j: every 4-lane quad reads one row's 64 contiguous
 //     bytes (one memory sector per quad, several times faster than a
 //     row-per-lane gather), and the swizzle keeps the later MFMA operand
 //     reads (row l%32, chunk c: slot 4r + (c ^ swz(r))) on distinct banks.
@@ -112,6 +114,22 @@ __device__ __forceinline__ void wait_vm_lgkm0()
     __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
 }
 
+// 16 bytes per lane from base + voff straight into LDS
+// (buffer_load_dwordx4 ... lds): lane l's bytes land at lds_dst + 16*l
+// (lds_dst wave-uniform). The buffer resource covers [base, base + 2 GiB)
+// with the gfx9-family raw-buffer configuration word, so offsets are 32-bit
+// and one past the range would read zeros rather than fault. The resource
+// type exists only in the device pass (the host pass would otherwise drop
+// the kernels' launch stubs).
+__device__ __forceinline__ void dma16(const void *base, int voff, void *lds_dst)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_dst, 16, voff, 0, 0, 0);
+#endif
+}
+
 __device__ __forceinline__ int tok_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
@@ -152,12 +170,13 @@ constexpr int cgcd(int a, int b) { return b == 0 ? a : cgcd(b, a % b); }
 constexpr int clcm(int a, int b) { return a / cgcd(a, b) * b; }
 
 // BM x BN output tile; WM row groups x WN column groups x WK k-groups of
-// wavefronts; token rows fetched LT stages ahead of their LDS write, weights
-// LW stages ahead of their use. WL: the weights go through LDS as well (in
-// the token pipeline, LT stages ahead of their LDS write), so that row
-// groups sharing a weight fragment (WM = 2) fetch it once; LW is then
-// unused. MP: memory instructions placed after each MFMA of a step's
-// interleave (int8; the e4m3 twin spreads them evenly over its MFMAs).
+// wavefronts; token images loaded into LDS LT stages ahead of the step that
+// reads them (a ring of LT+1 LDS stages), weights into registers LW stages
+// ahead of their use. WL: the weights go through LDS as well (whole images
+// in the token stages), so that row groups sharing a weight fragment
+// (WM = 2) fetch it once; LW is then unused. MP: memory instructions placed
+// after each MFMA of a step's interleave (int8; the e4m3 twin spreads them
+// evenly over its MFMAs).
 template <int BM_, int BN_, int WM_, int WN_, int WK_, int LT_, int LW_, bool WL_ = false,
           int MP_ = 1>
 struct Tile {
@@ -171,24 +190,23 @@ struct Tile {
     static constexpr int FN = BN / WN / 32;            // ... and columns
     static constexpr int AIMG = WK * MB;               // token images per stage
     static constexpr int WIMG = WLDS ? WK * (BN / 16) : 0;  // weight images per stage in LDS
-    static constexpr int LA = AIMG / NW;               // token loads per wave per stage
+    static constexpr int LA = AIMG / NW;               // token image loads per wave per stage
     static constexpr int LW8 = WIMG / NW;              // weight image loads per wave (LDS path)
-    static constexpr int LB = WLDS ? LW8 : 2 * FN;     // weight loads per wave per stage
-    static constexpr int LPW = LA + LB;                // global loads per wave per stage
-    static constexpr int NA = LT;                      // token staging register sets
+    static constexpr int LB = WLDS ? 0 : 2 * FN;       // weight register loads per wave per stage
+    static constexpr int LPW = LA + LW8 + LB;          // loads per wave per stage
+    static constexpr int NS = LT + 1;                  // LDS stages
     static constexpr int NB = WLDS ? 1 : LW + 1;       // weight register sets
-    static constexpr int GROUP = clcm(clcm(NA, NB), 2);     // steps per unrolled loop body
-    static constexpr int AHEAD = WLDS ? LT + 2 : cmax(LT + 2, LW);  // furthest stage fetched
-    // Steady-state wait at the top of a step: the token rows to be written
-    // to LDS (fetched LT steps earlier, first in their step) and the weights
-    // of this step (fetched LW steps earlier, last in their step) have landed.
-    // Through LDS, the weights of stage s+2 come right after its tokens.
+    static constexpr int GROUP = clcm(clcm(NB, 2), NS);     // steps per unrolled loop body
+    static constexpr int AHEAD = WLDS ? LT + 1 : cmax(LT + 1, LW);  // furthest stage fetched
+    // Steady-state wait at the top of step s: stage s+1's images (the first
+    // loads of step s-LT; on the LDS path the weight images follow the
+    // tokens) and the weights of stage s (the last loads of step s-LW) have
+    // landed.
     static constexpr int VM = WLDS ? (LT - 1) * LPW
-                                   : cmax(0, LB + (LT - 1) * LPW < (LW - 1) * LPW
-                                                 ? LB + (LT - 1) * LPW
-                                                 : (LW - 1) * LPW);
+                                   : (LB + (LT - 1) * LPW < (LW - 1) * LPW ? LB + (LT - 1) * LPW
+                                                                           : (LW - 1) * LPW);
     static constexpr int STAGE = (AIMG + WIMG) * 64;   // 16-byte slots per LDS stage
-    static constexpr int RING = 2 * STAGE * 16;        // two LDS stages, bytes
+    static constexpr int RING = NS * STAGE * 16;       // LDS ring, bytes
     static constexpr int PART = (WK - 1) * BM * BN * 4;     // k-group partial sums
     static constexpr int PITCH = BN * 2 + 16;          // staged bf16 row, bytes
     static constexpr int OUTB = BM * PITCH;
@@ -204,8 +222,9 @@ struct Tile {
     static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "tile/wave mismatch");
     static_assert(AIMG % NW == 0, "token loads must split evenly over waves");
     static_assert(WIMG % NW == 0, "weight image loads must split evenly over waves");
-    static_assert(LT >= 2 && LW >= LT, "token lead >= 2, weight lead >= token lead");
-    static_assert(VM < 64 && (LW + LT) * LPW < 64, "vmcnt range");
+    static_assert(LT >= 1 && (NS & (NS - 1)) == 0, "LDS ring of a power-of-two stages");
+    static_assert(WLDS || LW >= LT, "weight lead >= token lead");
+    static_assert(VM < 64 && (LT + 1) * LPW < 64 && (LW + 1) * LPW < 64, "vmcnt range");
     static_assert(LDS <= 160 * 1024, "LDS budget");
     static_assert(FM * FN * 16 <= 1024 / NW, "accumulators must leave room for operands");
     static_assert(WK <= 2 && FM % WK == 0, "k-groups split the row tiles evenly");
@@ -318,21 +337,11 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
         for (int i = 0; i < T::FM; ++i)
             acc[j][i] = Acc{};
     v4i bq[T::NB][T::FN][2];                           // weight operand ring (direct path)
-    v4i ast[T::NA][T::LA];                             // token staging ring
-    v4i bst[T::NA][T::LW8 > 0 ? T::LW8 : 1];           // weight image staging ring (LDS path)
     v4i xf[2][T::FM][2];                               // token operands, this and next stage
     v4i bf[T::WLDS ? 2 : 1][T::FN][2];                 // weight operands from LDS, this and next
 
-    // Global loads: token rows of stage t into staging set t % NA; weights of
-    // stage t into ring set t % NB. Addresses are clamped into the operands,
-    // so a load of a stage past the end is harmless.
-    auto load_a = [&](int t, v4i (&aset)[T::LA]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < T::LA; ++i) {
-            const int kc = min((t * T::WK + aks[i]) * 64 + dchunk, klast);
-            aset[i] = *reinterpret_cast<const v4i *>(arow[i] + kc);
-        }
-    };
+    // Weights of stage t into ring set t % NB. Addresses are clamped into
+    // the operands, so a load of a stage past the end is harmless.
     auto load_b = [&](int t, v4i (&bset)[T::FN][2]) __attribute__((always_inline)) {
         const int kb = min(t * T::WK + wk, kblast);
 #pragma unroll
@@ -341,35 +350,41 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
             for (int h = 0; h < 2; ++h)
                 bset[j][h] = bsrc[j][(int64_t)kb * 64 + h * 32];
     };
-    // LDS path: whole 1 KB weight images of stage t (image g = i*NW + wave of
-    // the stage is k-block g / (BN/16), channel image g % (BN/16) of the
-    // tile), one coalesced 16-byte load per lane.
-    auto load_w = [&](int t, v4i (&wset)[T::LW8 > 0 ? T::LW8 : 1]) __attribute__((always_inline)) {
+    // The token images (and, on the LDS path, the weight images) of stage t
+    // straight from memory into LDS stage t % NS: image g of the stage to its
+    // 1 KB slot, lane l to 16-byte slot l. Token image g = i*NW + wave is
+    // k-block g / MB of the stage, rows 16*(g % MB) ..; weight image g is
+    // k-block g / (BN/16), channel image g % (BN/16) of the tile. Offsets are
+    // from the tile's first token row and first weight image (32-bit).
+    // Addresses are clamped into the operands, so a load of a stage past the
+    // end is harmless.
+    const int8_t *xb = a.xq + (int64_t)m0 * a.ldq;
+    const char *wb = reinterpret_cast<const char *>(a.wp) + (int64_t)(n0 / 16) * a.kblocks * 1024;
+    int aoff[T::LA];
+#pragma unroll
+    for (int i = 0; i < T::LA; ++i)
+        aoff[i] = (int)(arow[i] - xb);
+    auto dma = [&](int t) __attribute__((always_inline)) {
+        char *st = reinterpret_cast<char *>(lds) + (t & (T::NS - 1)) * T::STAGE * 16;
+#pragma unroll
+        for (int i = 0; i < T::LA; ++i) {
+            const int g = i * T::NW + wave;
+            const int kc = min((t * T::WK + aks[i]) * 64 + dchunk, klast);
+            dma16(xb, aoff[i] + kc, st + g * 1024);
+        }
 #pragma unroll
         for (int i = 0; i < T::LW8; ++i) {
             const int g = i * T::NW + wave;
             const int kb = min(t * T::WK + g / (T::BN / 16), kblast);
-            const int img = min(n0 / 16 + g % (T::BN / 16), a.nblocks - 1);
-            wset[i] = reinterpret_cast<const v4i *>(a.wp)[((int64_t)img * a.kblocks + kb) * 64 + lane];
+            const int img = min(n0 / 16 + g % (T::BN / 16), a.nblocks - 1) - n0 / 16;
+            dma16(wb, (img * a.kblocks + kb) * 1024 + lane * 16, st + (T::AIMG + g) * 1024);
         }
-    };
-    // Token rows (and, on the LDS path, weight images) of stage t from
-    // staging registers into LDS stage t % 2.
-    auto store = [&](int t, const v4i (&aset)[T::LA], const v4i (&wset)[T::LW8 > 0 ? T::LW8 : 1])
-                     __attribute__((always_inline)) {
-        v4i *st = reinterpret_cast<v4i *>(lds) + (t & 1) * T::STAGE;
-#pragma unroll
-        for (int i = 0; i < T::LA; ++i)
-            st[(i * T::NW + wave) * 64 + lane] = aset[i];
-#pragma unroll
-        for (int i = 0; i < T::LW8; ++i)
-            st[(T::AIMG + i * T::NW + wave) * 64 + lane] = wset[i];
     };
     // LDS path: this wave's weight operands of stage t (its k-group's
     // k-block): for 32-channel group j the images 2*(wn*FN+j) + (l>>4 & 1),
     // slot 16*(2h + l/32) + l%16, as the direct path loads them.
     auto bread = [&](int t, v4i (&b)[T::FN][2]) __attribute__((always_inline)) {
-        const v4i *st = reinterpret_cast<const v4i *>(lds) + (t & 1) * T::STAGE +
+        const v4i *st = reinterpret_cast<const v4i *>(lds) + (t & (T::NS - 1)) * T::STAGE +
                         (T::AIMG + wk * (T::BN / 16)) * 64;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -380,7 +395,7 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
     };
     // This wave's token operands of stage t (its k-group's k-block) from LDS.
     auto read = [&](int t, v4i (&x)[T::FM][2]) __attribute__((always_inline)) {
-        const v4i *st = reinterpret_cast<const v4i *>(lds) + (t & 1) * T::STAGE + wk * T::MB * 64 +
+        const v4i *st = reinterpret_cast<const v4i *>(lds) + (t & (T::NS - 1)) * T::STAGE + wk * T::MB * 64 +
                         wm * (2 * T::FM) * 64;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -416,27 +431,30 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
     // times as many, measured on MI355X); the e4m3 twin has half as many
     // (twice as long) MFMAs, so its memory instructions are spread over them.
     constexpr int DS_READS = 2 * T::FM + (T::WLDS ? 2 * T::FN : 0);
-    constexpr int DS_WRITES = T::LA + T::LW8;
-    constexpr int MEM_OPS = DS_READS + DS_WRITES + T::LPW;
+    constexpr int MEM_OPS = DS_READS + T::LPW;
     constexpr int PER = FP8 ? (MEM_OPS + NMMA - PRE - 1) / (NMMA - PRE) : T::MP;
 
-    // Step s. On entry stage s+1 is being written to LDS by every wave, this
-    // wave's operands of stage s are in xf[s & 1], token rows of stage s+2
-    // sit in staging set (s+2) % NA and the weights of stage s in ring set
-    // s % NB. The step: the first MFMAs of stage s (they keep the matrix
-    // core busy across the barrier), barrier (stage s+1 visible; every read
-    // of stage s done), read stage s+1's operands, write stage s+2 to the LDS
-    // buffer stage s used, fetch tokens of stage s+2+LT and weights of stage
-    // s+LW, interleaved (PER at a time) with the rest of stage s's MFMAs so that
-    // they issue while the matrix core is busy.
+    // Step s. On entry this wave's operands of stage s are in xf[s & 1], the
+    // images of stages s+1 .. s+LT are landing in LDS and the weights of
+    // stage s are in ring set s % NB. The step: wait until stage s+1's images
+    // and stage s's weights have landed; the first MFMAs of stage s (they keep
+    // the matrix core busy across the barrier); barrier (stage s+1 visible to
+    // every wave; every read of stage s done); read stage s+1's operands; load
+    // stage s+1+LT's images into the LDS stage that stage s used and the
+    // weights of stage s+LW, interleaved (PER at a time) with the rest of
+    // stage s's MFMAs so that they issue while the matrix core is busy.
+    // The compiler does not order LDS reads after these loads: the explicit
+    // waits and the barrier do.
     auto step = [&](auto full, int s, auto u_c) __attribute__((always_inline)) {
         constexpr bool FULL = decltype(full)::value;
         constexpr int u = decltype(u_c)::value;        // s modulo GROUP
         const bool run = FULL || s * T::WK + wk < a.kblocks;
+        // The steady state waits for exactly what it needs; the last steps
+        // (where fewer loads follow) drain.
         if (FULL)
             wait_vm_lgkm0<T::VM>();
         else
-            wait_lgkm0();
+            wait_vm_lgkm0<0>();
         auto &wcur = [&]() -> auto & {
             if constexpr (T::WLDS)
                 return bf[u & 1];
@@ -451,13 +469,8 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
             if constexpr (T::WLDS)
                 bread(s + 1, bf[(u + 1) & 1]);
         }
-        if (FULL || s + 2 < S)
-            store(s + 2, ast[(u + 2) % T::NA], bst[(u + 2) % T::NA]);
-        if (FULL || s + 2 + T::LT < S) {
-            load_a(s + 2 + T::LT, ast[(u + 2) % T::NA]);
-            if constexpr (T::WLDS)
-                load_w(s + 2 + T::LT, bst[(u + 2) % T::NA]);
-        }
+        if (FULL || s + 1 + T::LT < S)
+            dma(s + 1 + T::LT);
         if constexpr (!T::WLDS) {
             if (FULL || s + T::LW < S)
                 load_b(s + T::LW, bq[(u + T::LW) % T::NB]);
@@ -465,10 +478,8 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
         if (run)
             mma(std::integral_constant<int, PRE>{}, std::integral_constant<int, NMMA>{}, xf[u & 1], wcur);
         if (FULL) {
-            // PER memory instructions after each MFMA: operand reads first,
-            // then the global loads, then the LDS writes (2-3 % faster on the
-            // 256-row tiles than the writes before the loads, the same on
-            // the others).
+            // PER memory instructions after each MFMA: the operand reads
+            // first, then the loads.
             static_for<(DS_READS + PER - 1) / PER>([&](auto) __attribute__((always_inline)) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x100, PER, 0); // DS read
@@ -476,10 +487,6 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
             static_for<(T::LPW + PER - 1) / PER>([&](auto) __attribute__((always_inline)) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x020, PER, 0); // VMEM read
-            });
-            static_for<(DS_WRITES + PER - 1) / PER>([&](auto) __attribute__((always_inline)) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x200, PER, 0); // DS write
             });
         }
         // Keep each step's loads in program order relative to the next
@@ -539,34 +546,26 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
         }
     }
 
-    // Prologue: stages 0 and 1 into LDS, stage 0's operands into xf[0], and
-    // the loads that steps -LT .. -1 would have issued. Every load is issued
-    // even when its stage does not exist, so the load counter state at the
-    // loop entry matches the one at the back-edge and the waits the
-    // compiler derives inside the loop stay as loose as the steady state.
-    load_a(0, ast[0]);
-    if constexpr (T::WLDS)
-        load_w(0, bst[0]);
-    load_a(1, ast[1 % T::NA]);
-    if constexpr (T::WLDS) {
-        load_w(1, bst[1 % T::NA]);
-    } else {
+    // Prologue: the weights of the stages before the first virtual step's,
+    // stage 0's images, then the loads that steps -LT .. -1 would have
+    // issued, then stage 0's operands into xf[0]. Every load is issued even
+    // when its stage does not exist (its addresses are clamped and its LDS
+    // stage is never read), so the load counter state at the loop entry
+    // matches the one at the back-edge. Stage 0 has landed once no more than
+    // the virtual steps' loads are in flight.
+    if constexpr (!T::WLDS)
         static_for<T::LW - T::LT>([&](auto U) __attribute__((always_inline)) {
             constexpr int t = decltype(U)::value;
             load_b(t, bq[t % T::NB]);
         });
-    }
-    store(0, ast[0], bst[0]);
-    store(1, ast[1 % T::NA], bst[1 % T::NA]);
+    dma(0);
     static_for<T::LT>([&](auto U) __attribute__((always_inline)) {
         constexpr int v = decltype(U)::value - T::LT;  // virtual step -LT .. -1
-        load_a(v + 2 + T::LT, ast[(v + 2 + T::LT) % T::NA]);
-        if constexpr (T::WLDS)
-            load_w(v + 2 + T::LT, bst[(v + 2 + T::LT) % T::NA]);
-        else
+        dma(v + 1 + T::LT);
+        if constexpr (!T::WLDS)
             load_b(v + T::LW, bq[(v + T::LW) % T::NB]);
     });
-    wait_lgkm0();
+    wait_vm_lgkm0<T::LT * T::LPW>();
     __builtin_amdgcn_s_barrier();
     read(0, xf[0]);
     if constexpr (T::WLDS)
@@ -612,7 +611,7 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
                     side[p] = side_v[u];
             }
         }
-        wait_lgkm0();
+        wait_vm_lgkm0<0>();                            // no image still landing in the ring
         __builtin_amdgcn_s_barrier();                  // every wave is done with the ring
 
         // Hand over the partial sums of the other k-group's rows: one 16-byte
@@ -785,16 +784,16 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
 // The main kernel's tile configurations in tile-number order (the int8
 // kernel and its e4m3 twin use the same list): BM x BN output tile / WM row
 // groups x WN column groups x WK k-groups of waves / token and weight fetch
-// leads in stages ("l2lds": weights through LDS in the token pipeline, two
+// leads in stages ("l3lds": weights through LDS with the tokens, three
 // stages ahead; measured on MI355X 6-9 % faster than fetching them straight
 // into registers, where the two row groups each load every fragment).
-using MainTiles = std::tuple<Tile<64, 64, 1, 2, 2, 2, 3>, Tile<64, 128, 1, 2, 2, 2, 3, false, 2>,
-                             Tile<128, 64, 1, 2, 2, 2, 3, false, 3>, Tile<128, 128, 1, 2, 2, 2, 3>,
-                             Tile<128, 192, 1, 2, 2, 2, 3>, Tile<256, 128, 2, 2, 1, 2, 3, true, 2>,
-                             Tile<256, 192, 2, 2, 1, 2, 3, true>>;
+using MainTiles = std::tuple<Tile<64, 64, 1, 2, 2, 3, 3>, Tile<64, 128, 1, 2, 2, 3, 3, false, 2>,
+                             Tile<128, 64, 1, 2, 2, 3, 3, false, 3>, Tile<128, 128, 1, 2, 2, 3, 3>,
+                             Tile<128, 192, 1, 2, 2, 3, 3>, Tile<256, 128, 2, 2, 1, 3, 3, true, 2>,
+                             Tile<256, 192, 2, 2, 1, 3, 3, true>>;
 constexpr const char *kMainTileNames[] = {
-    "64x64/m1n2k2/l23",   "64x128/m1n2k2/l23",    "128x64/m1n2k2/l23",    "128x128/m1n2k2/l23",
-    "128x192/m1n2k2/l23", "256x128/m2n2k1/l2lds", "256x192/m2n2k1/l2lds"};
+    "64x64/m1n2k2/l33",   "64x128/m1n2k2/l33",    "128x64/m1n2k2/l33",    "128x128/m1n2k2/l33",
+    "128x192/m1n2k2/l33", "256x128/m2n2k1/l3lds", "256x192/m2n2k1/l3lds"};
 constexpr int kNumMainTiles = (int)std::tuple_size<MainTiles>::value;
 static_assert(sizeof(kMainTileNames) / sizeof(kMainTileNames[0]) == kNumMainTiles, "tile names");
 
