@@ -208,6 +208,28 @@ def test_scaled_mm_i32_every_tile(ops, orc, M, N, K):
         assert np.array_equal(acc.cpu().numpy(), ref), f"tile {ops.tile_name(t)}"
 
 
+# K values giving every number of LDS stages from 1 to 20 on the tiles with one
+# k-group (a stage is one 64-deep k-block) and 1 to 10 on those with two (two
+# k-blocks per stage), with a partial last k-block in between: the main
+# kernel's LDS ring holds four stages, and loads for stages past the end are
+# still issued (to clamped addresses) when K is short.
+RING_KS = [64 * s for s in range(1, 21)] + [16, 208, 464, 720]
+
+
+@pytest.mark.parametrize("K", RING_KS)
+def test_scaled_mm_i32_ring_depths_every_tile(ops, orc, K):
+    M, N = 97, 130
+    rng = np.random.default_rng(4500 + K)
+    xq = rand_i8(rng, (M, K), lo=-128)
+    wq = rand_i8(rng, (N, K), lo=-128)
+    ref = orc.gemm_i32(xq, wq)
+    xq_d = torch.from_numpy(xq).to(DEV)
+    packed = ops.prepack_weight(torch.from_numpy(wq).to(DEV))
+    for t in _ntiles(ops):
+        acc = ops.scaled_mm(xq_d, None, packed, None, N, out_dtype=torch.int32, tile=t)
+        assert np.array_equal(acc.cpu().numpy(), ref), f"tile {ops.tile_name(t)} K {K}"
+
+
 @pytest.mark.parametrize("M,N,K", SHAPES)
 @pytest.mark.parametrize("bias", [False, True])
 def test_scaled_mm_bf16_every_tile(ops, orc, M, N, K, bias):
@@ -418,7 +440,7 @@ def test_workload_full_size(ops, orc, name):
 # fits the device, two launches otherwise)
 # ---------------------------------------------------------------------------
 QMM_SHAPES = [(1, 48, 64), (37, 45, 80), (130, 200, 336), (257, 300, 1040), (512, 520, 576),
-              (512, 1536, 512), (2, 1000, 4112), (1, 300, 16384)]
+              (512, 1536, 512), (2, 1000, 4112), (1, 300, 16384), (97, 130, 192), (66, 200, 448)]
 
 
 @pytest.mark.parametrize("M,N,K", QMM_SHAPES)
