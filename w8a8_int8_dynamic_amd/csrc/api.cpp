@@ -412,9 +412,9 @@ w8a8_status_t quant_mm_common(const uint16_t *x, int x_kind, int64_t ldx, int8_t
         (void)hipGetLastError();
     }
     // Two launches on the same stream (also when the grid cannot be
-    // resident all at once).
+    // resident all at once); the codes stay in the caches for the matmul.
     a.x = nullptr;
-    hipError_t err = w8a8::launch_quant_rows(x, x_kind, M, K, ldx, xq, ldq, x_scale, s);
+    hipError_t err = w8a8::launch_quant_rows(x, x_kind, M, K, ldx, xq, ldq, x_scale, s, false, true);
     if (err != hipSuccess)
         return launched(err, what);
     return launched(w8a8::launch_scaled_mm(a, mode, t, s), what);
@@ -628,7 +628,8 @@ W8A8_API w8a8_status_t fp8_quant_scaled_mm_tile(const uint16_t *x, int64_t ldx, 
         a.x = nullptr;
     }
     hipError_t err = w8a8::launch_quant_rows(x, w8a8::kElemBF16, M, K, ldx,
-                                             reinterpret_cast<int8_t *>(xq), ldq, x_scale, s, true);
+                                             reinterpret_cast<int8_t *>(xq), ldq, x_scale, s, true,
+                                             true);
     if (err != hipSuccess)
         return launched(err, what);
     return launched(w8a8::launch_scaled_mm_fp8(a, mode, t, s), what);

@@ -31,10 +31,12 @@ constexpr int kElemBF16 = 0, kElemF32 = 1, kElemF16 = 2;
 
 // ---- per-row quantization (quant.hip) ----
 // kind: x is bf16 bits, fp32 or fp16 bits [rows, ldx]. fp8: e4m3 codes
-// (bf16 or fp32 rows only) instead of int8.
+// (bf16 or fp32 rows only) instead of int8. keep_codes: the codes are read
+// by the next launch, so they are stored to stay in the caches (activation
+// rows only; otherwise they are streamed out).
 hipError_t launch_quant_rows(const void *x, int kind, int64_t rows, int64_t K, int64_t ldx,
                              int8_t *q, int64_t ldq, float *scale, hipStream_t stream,
-                             bool fp8 = false);
+                             bool fp8 = false, bool keep_codes = false);
 
 // ---- weight repack (prepack.hip) ----
 hipError_t launch_prepack(const int8_t *wq, int64_t N, int64_t K, int64_t ldw, void *packed,

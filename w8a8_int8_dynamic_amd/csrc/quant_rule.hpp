@@ -160,17 +160,26 @@ __device__ __forceinline__ uint4 load_chunk(const char *row, int64_t e, int K)
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-template <int E>
+// STREAM: the codes are written with nontemporal stores (nothing reads them
+// soon); otherwise with plain stores, so that they stay in the caches for
+// the launch that reads them next.
+template <int E, bool STREAM = true>
 __device__ __forceinline__ void store_codes(int8_t *qrow, int64_t e, int K, u32 lo, u32 hi)
 {
     constexpr bool F32 = E == kF32;
     constexpr int VEC = Elem<E>::VEC;
     if (e + VEC <= K) {
-        // The codes are not read again by this pass: stream them out.
-        if (F32)
-            __builtin_nontemporal_store(lo, reinterpret_cast<u32 *>(qrow + e));
-        else
-            __builtin_nontemporal_store(v2u{lo, hi}, reinterpret_cast<v2u *>(qrow + e));
+        if constexpr (STREAM) {
+            if (F32)
+                __builtin_nontemporal_store(lo, reinterpret_cast<u32 *>(qrow + e));
+            else
+                __builtin_nontemporal_store(v2u{lo, hi}, reinterpret_cast<v2u *>(qrow + e));
+        } else {
+            if (F32)
+                *reinterpret_cast<u32 *>(qrow + e) = lo;
+            else
+                *reinterpret_cast<v2u *>(qrow + e) = v2u{lo, hi};
+        }
         return;
     }
     for (int j = 0; j < VEC; ++j)
