@@ -790,14 +790,18 @@ __global__ __launch_bounds__(T::THREADS) void scaled_mm_kernel(const MmArgs args
 // groups x WN column groups x WK k-groups of waves / token and weight fetch
 // leads in stages ("l3lds": weights through LDS with the tokens, three
 // stages ahead; measured on MI355X 6-9 % faster than fetching them straight
-// into registers, where the two row groups each load every fragment).
+// into registers, where the two row groups each load every fragment). The
+// 256x256 tile takes all 512 registers of a lane (256 of them accumulators;
+// its epilogue spills 8 bytes) and 138 KB of LDS; it reads the fewest L2
+// bytes per MFMA op of the list and wins on large shapes whose tiles fill
+// whole rounds of 256 CUs.
 using MainTiles = std::tuple<Tile<64, 64, 1, 2, 2, 3, 3>, Tile<64, 128, 1, 2, 2, 3, 3, false, 2>,
                              Tile<128, 64, 1, 2, 2, 3, 3, false, 3>, Tile<128, 128, 1, 2, 2, 3, 3>,
                              Tile<128, 192, 1, 2, 2, 3, 3>, Tile<256, 128, 2, 2, 1, 3, 3, true, 2>,
-                             Tile<256, 192, 2, 2, 1, 3, 3, true>>;
+                             Tile<256, 192, 2, 2, 1, 3, 3, true>, Tile<256, 256, 2, 2, 1, 3, 3, true>>;
 constexpr const char *kMainTileNames[] = {
     "64x64/m1n2k2/l33",   "64x128/m1n2k2/l33",    "128x64/m1n2k2/l33",    "128x128/m1n2k2/l33",
-    "128x192/m1n2k2/l33", "256x128/m2n2k1/l3lds", "256x192/m2n2k1/l3lds"};
+    "128x192/m1n2k2/l33", "256x128/m2n2k1/l3lds", "256x192/m2n2k1/l3lds", "256x256/m2n2k1/l3lds"};
 constexpr int kNumMainTiles = (int)std::tuple_size<MainTiles>::value;
 static_assert(sizeof(kMainTileNames) / sizeof(kMainTileNames[0]) == kNumMainTiles, "tile names");
 
