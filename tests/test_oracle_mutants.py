@@ -62,6 +62,22 @@ MUTANTS = {
     "fp8_subnormal_boundary": ("if (exp_unbiased < -6)", "if (exp_unbiased < -7)"),
     "fp8_scale_by_reciprocal": ("float s = a / 448.0f;", "float s = a * (1.0f / 448.0f);"),
     "fp8_codes_by_divide": ("float t = v[k] * inv;\n        if (t > 448.0f)", "float t = v[k] / s;\n        if (t > 448.0f)"),
+    "int8_scale_by_reciprocal": ("float s = a / 127.0f;", "float s = a * (1.0f / 127.0f);"),
+    "int8_codes_by_divide": ("float t = v[k] * inv;\n        t = rintf(t);",
+                             "float t = v[k] / s;\n        t = rintf(t);"),
+    "int8_inv_from_scale": ("float inv = 127.0f / a;", "float inv = 1.0f / s;"),
+    "absmax_skips_first": ("for (int64_t k = 0; k < K; ++k) {\n        float m = fabsf(v[k]);",
+                           "for (int64_t k = 1; k < K; ++k) {\n        float m = fabsf(v[k]);"),
+    "gemm_skips_first_k": ("for (int64_t k = 0; k < K; ++k)\n                s += (int64_t)ar[k]",
+                           "for (int64_t k = 1; k < K; ++k)\n                s += (int64_t)ar[k]"),
+    "bias_before_w_scale": ("t = t * ws[n];\n            if (bias)\n                t = t + bf16_bits_to_float(bias[n]);\n"
+                            "            out[m * ldo + n] = float_to_bf16_rne(t);",
+                            "if (bias)\n                t = t + bf16_bits_to_float(bias[n]);\n            t = t * ws[n];\n"
+                            "            out[m * ldo + n] = float_to_bf16_rne(t);"),
+    "acc_transposed_index": ("float t = (float)acc[m * ldc + n];\n            t = t * xs[m];\n            t = t * ws[n];\n"
+                             "            if (bias)\n                t = t + bf16_bits_to_float(bias[n]);",
+                             "float t = (float)acc[(n % M) * ldc + (m % N)];\n            t = t * xs[m];\n"
+                             "            t = t * ws[n];\n            if (bias)\n                t = t + bf16_bits_to_float(bias[n]);"),
     "fp8_no_zero_row_rule": ("if (a < 0x1p-100f) {\n        *scale = 0.0f;\n        for (int64_t k = 0; k < K; ++k)\n            q[k] = 0;\n        return;\n    }\n    float s = a / 448.0f;",
                              "if (a < 0.0f) {\n        *scale = 0.0f;\n        for (int64_t k = 0; k < K; ++k)\n            q[k] = 0;\n        return;\n    }\n    float s = a / 448.0f;"),
 }
